@@ -1,0 +1,198 @@
+"""MI355X (gfx950) MoE FP8 training hot path: fused FP8 quantization and scaled grouped GEMM.
+
+Thin ctypes binding over the C ABI in ``include/fp8_quant_grouped.h`` (library
+``libfp8qg.so`` next to this file, built by ``_build.build()``).  Each Python function has the
+name of the C entry point it calls and only marshals arguments: it takes torch tensors for
+device memory, allocates outputs with torch on the input's device, passes raw pointers and the
+current HIP stream, and raises on a non-zero status.  Every step of the computation runs in
+the HIP kernels; there is no fallback.  If the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfp8qg.so")
+
+E4M3FNUZ = 0  # AMD e4m3fnuz: largest value 240
+E4M3FN = 1    # OCP e4m3fn: largest value 448
+FMAX = {E4M3FNUZ: 240.0, E4M3FN: 448.0}
+GEMM_FWD_MGROUPED = 0
+GEMM_WGRAD_KGROUPED = 1
+
+_lib = None
+
+# name -> (restype, argtypes)
+_P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+_I = ctypes.c_int
+SIGNATURES = {
+    "fp8q_abi_version": (_I, []),
+    "fp8q_status_string": (ctypes.c_char_p, [_I]),
+    "fp8_quant_rowwise": (_I, [_P, _I64, _I64, _I64, _I, _P, _I64, _P, _P]),
+    "fp8_quant_colwise_grouped_workspace_size": (_SZ, [_I64, _I64, _I32]),
+    "fp8_quant_colwise_grouped": (_I, [_P, _I64, _I64, _I64, _P, _I32, _I, _P, _I64, _P, _P, _SZ,
+                                       _P]),
+    "fp8_grouped_gemm": (_I, [_I, _I, _P, _I64, _P, _P, _I64, _I64, _P, _P, _I32, _I64, _I64,
+                              _I64, _P, _I64, _P]),
+    "fp8_mx_quant_rowwise": (_I, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P]),
+    "fp8_mx_quant_colwise": (_I, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P]),
+    "fp8_mx_grouped_gemm": (_I, [_P, _I64, _P, _I64, _P, _I64, _I64, _P, _I64, _I64, _P, _I32,
+                                 _I64, _I64, _I64, _P, _I64, _P]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "fp8_quantization_grouped_amd._build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(name: str, status: int) -> None:
+    if status != 0:
+        msg = lib().fp8q_status_string(status).decode()
+        raise RuntimeError(f"{name} failed: status {status} ({msg})")
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, what: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+
+
+def fp8_quant_rowwise(x: torch.Tensor, fmt: int, q: torch.Tensor | None = None,
+                      scales: torch.Tensor | None = None):
+    """x: bf16 [rows, cols] (row stride may exceed cols).  Returns (q uint8 [rows, cols],
+    scales float32 [rows])."""
+    _dev(x, "x")
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    st = lib().fp8_quant_rowwise(_ptr(x), rows, cols, x.stride(0), fmt, _ptr(q), q.stride(0),
+                                 _ptr(scales), _stream(x))
+    _check("fp8_quant_rowwise", st)
+    return q, scales
+
+
+def fp8_quant_colwise_grouped_workspace_size(rows: int, cols: int, groups: int) -> int:
+    return int(lib().fp8_quant_colwise_grouped_workspace_size(rows, cols, groups))
+
+
+def fp8_quant_colwise_grouped(x: torch.Tensor, offsets: torch.Tensor, fmt: int,
+                              q_t: torch.Tensor | None = None,
+                              scales: torch.Tensor | None = None,
+                              workspace: torch.Tensor | None = None):
+    """x: bf16 [rows, cols]; offsets: int32 device [groups] (cumulative group ends).
+    Returns (q_t uint8 [cols, rows] column-major copy, scales float32 [groups, cols])."""
+    _dev(x, "x")
+    _dev(offsets, "offsets")
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    assert offsets.dtype == torch.int32 and offsets.is_contiguous()
+    rows, cols = x.shape
+    groups = offsets.numel()
+    if q_t is None:
+        q_t = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((groups, cols), dtype=torch.float32, device=x.device)
+    need = fp8_quant_colwise_grouped_workspace_size(rows, cols, groups)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=x.device)
+    st = lib().fp8_quant_colwise_grouped(_ptr(x), rows, cols, x.stride(0), _ptr(offsets), groups,
+                                         fmt, _ptr(q_t), q_t.stride(0), _ptr(scales),
+                                         _ptr(workspace), workspace.numel(), _stream(x))
+    _check("fp8_quant_colwise_grouped", st)
+    return q_t, scales
+
+
+def fp8_grouped_gemm(mode: int, fmt: int, a: torch.Tensor, a_scales: torch.Tensor,
+                     b: torch.Tensor, b_scales: torch.Tensor, offsets: torch.Tensor, M: int,
+                     N: int, K: int, ldb: int | None = None, b_group_stride: int = 0,
+                     c: torch.Tensor | None = None):
+    """Scaled FP8 grouped GEMM (see the C header for the two modes).
+    Forward: a [M, lda], b holds every group's [N, K] rows at ldb / b_group_stride; returns
+    bf16 [M, N].  Weight gradient: a [K, lda >= M], b [N, ldb >= M]; returns bf16 [G, K, N]."""
+    _dev(a, "a")
+    groups = offsets.numel()
+    if ldb is None:
+        ldb = b.stride(0)
+    if c is None:
+        shape = (M, N) if mode == GEMM_FWD_MGROUPED else (groups, K, N)
+        c = torch.empty(shape, dtype=torch.bfloat16, device=a.device)
+    ldc = c.stride(-2)
+    st = lib().fp8_grouped_gemm(mode, fmt, _ptr(a), a.stride(0), _ptr(a_scales), _ptr(b), ldb,
+                                b_group_stride, _ptr(b_scales), _ptr(offsets), groups, M, N, K,
+                                _ptr(c), ldc, _stream(a))
+    _check("fp8_grouped_gemm", st)
+    return c
+
+
+def fp8_mx_quant_rowwise(x: torch.Tensor, q: torch.Tensor | None = None,
+                         e8m0: torch.Tensor | None = None):
+    """Returns (q uint8 [rows, cols] OCP e4m3fn, e8m0 uint8 [rows, cols/32])."""
+    _dev(x, "x")
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if e8m0 is None:
+        e8m0 = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    st = lib().fp8_mx_quant_rowwise(_ptr(x), rows, cols, x.stride(0), _ptr(q), q.stride(0),
+                                    _ptr(e8m0), e8m0.stride(0), _stream(x))
+    _check("fp8_mx_quant_rowwise", st)
+    return q, e8m0
+
+
+def fp8_mx_quant_colwise(x: torch.Tensor, q_t: torch.Tensor | None = None,
+                         e8m0: torch.Tensor | None = None):
+    """Blocks of 32 rows per column, transposed output.  Returns (q_t uint8 [cols, rows],
+    e8m0 uint8 [cols, rows/32])."""
+    _dev(x, "x")
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    rows, cols = x.shape
+    if q_t is None:
+        q_t = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    if e8m0 is None:
+        e8m0 = torch.empty((cols, rows // 32), dtype=torch.uint8, device=x.device)
+    st = lib().fp8_mx_quant_colwise(_ptr(x), rows, cols, x.stride(0), _ptr(q_t), q_t.stride(0),
+                                    _ptr(e8m0), e8m0.stride(0), _stream(x))
+    _check("fp8_mx_quant_colwise", st)
+    return q_t, e8m0
+
+
+def fp8_mx_grouped_gemm(a: torch.Tensor, a_e8m0: torch.Tensor, b: torch.Tensor,
+                        b_e8m0: torch.Tensor, offsets: torch.Tensor, M: int, N: int, K: int,
+                        ldb: int, b_group_stride: int, ld_sb: int, sb_group_stride: int,
+                        c: torch.Tensor | None = None):
+    """MX grouped GEMM forward; returns bf16 [M, N]."""
+    _dev(a, "a")
+    groups = offsets.numel()
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    st = lib().fp8_mx_grouped_gemm(_ptr(a), a.stride(0), _ptr(a_e8m0), a_e8m0.stride(0), _ptr(b),
+                                   ldb, b_group_stride, _ptr(b_e8m0), ld_sb, sb_group_stride,
+                                   _ptr(offsets), groups, M, N, K, _ptr(c), c.stride(0),
+                                   _stream(a))
+    _check("fp8_mx_grouped_gemm", st)
+    return c

@@ -1,0 +1,184 @@
+/*
+ * fp8_quant_grouped.h -- C ABI of the MI355X (gfx950) MoE FP8 training hot path.
+ *
+ * Operations (page titles as printed on the pages they come from):
+ *   - "FP8 su GPU AMD: i guadagni di TorchTitan e TorchAO ora sono nel mainline PyTorch"
+ *     (ai-radar.it), introduction: MoE FP8 training needs rowwise scales on activations,
+ *     columnwise scales on the expert weights and an offset tensor that routes tokens to
+ *     experts.  Section "La correttezza del formato viene prima del tuning": AMD's e4m3fnuz
+ *     format has 240 as its largest value and no NaN/Inf encoding; scales must be taken
+ *     against the maximum of the format actually used.  Section "Il guadagno vero e' nel
+ *     movimento dei dati": the chain is absmax per row or column, scale, clamp, cast to FP8;
+ *     the backward's transposed operand is written directly (no transpose-copy through HBM);
+ *     columnwise outputs are transposed through LDS so that writes coalesce; cross-block
+ *     maxima use relaxed-order atomics.
+ *   - "AMD Boosts PyTorch FP8 Training on Instinct GPUs" (latestnews.news), third paragraph:
+ *     FNUZ is "finite, no NaN, unsigned zero"; grouped GEMM for MoE on ROCm.
+ *   - "AMD Primus adds FP8/MXFP8 kernels, megakernel fusion and DeepSeek-V3 training at 1024
+ *     GPUs" (fosswire.org), section "What Primus adds for MoE training on MI355X": FP8 and
+ *     MXFP8 grouped GEMM for expert FFNs.  MXFP8 itself (1x32 blocks, E8M0 power-of-two
+ *     shared scale, e4m3 elements) is defined by the OCP Microscaling Formats v1.0 spec.
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument is a DEVICE pointer owned by the caller; the library never
+ *     allocates, frees or retains memory.  bf16 tensors are passed as raw 16-bit patterns.
+ *   - Every call is asynchronous on `stream` (0 = the null stream) and never synchronises the
+ *     host.  Offsets tensors are read on the device only.
+ *   - Matrices are row-major with an explicit leading dimension (elements between rows).
+ *   - Offsets: int32[groups], the cumulative END row of each group: group g covers rows
+ *     [offsets[g-1], offsets[g]) with offsets[-1] = 0.  Non-decreasing, offsets[groups-1] equals
+ *     the row count, empty groups allowed.  Violations are undefined behaviour (not checked).
+ *   - Inputs must be finite.  Behaviour on NaN/Inf inputs is unspecified.
+ *   - Host-checkable violations (null pointer, negative size, leading dimension too small,
+ *     unknown format, workspace too small, a size beyond a kernel's limit) return a status
+ *     and launch nothing.  A failed launch returns FP8Q_ERR_HIP.
+ *   - Scale semantics: the stored scale is the quantization MULTIPLIER
+ *     s = FMAX / max(absmax, 1e-12f), rounded once to fp32; dequantization multiplies by 1/s.
+ *     Elements are cast as q = ENC(clamp(RN32(x * s), -FMAX, FMAX)) with round-to-nearest-even
+ *     into the FP8 grid.  e4m3fnuz never yields byte 0x80 (its NaN); any value that rounds to
+ *     zero gives 0x00.  e4m3fn keeps the sign of zero.
+ */
+#ifndef FP8_QUANT_GROUPED_H
+#define FP8_QUANT_GROUPED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+#define FP8Q_ABI_VERSION 1
+
+/* FP8 element encoding.  e4m3fnuz: bias 8, largest value 240, single zero, 0x80 is NaN
+ * ("La correttezza del formato viene prima del tuning").  e4m3fn: OCP e4m3, bias 7, largest
+ * value 448, signed zero, 0x7F/0xFF are NaN. */
+typedef enum { FP8Q_E4M3FNUZ = 0, FP8Q_E4M3FN = 1 } fp8q_format_t;
+
+typedef enum {
+    FP8Q_OK = 0,
+    FP8Q_ERR_INVALID_ARG = 1,
+    FP8Q_ERR_UNSUPPORTED = 2,
+    FP8Q_ERR_WORKSPACE = 3,
+    FP8Q_ERR_HIP = 4
+} fp8q_status_t;
+
+typedef enum { FP8Q_GEMM_FWD_MGROUPED = 0, FP8Q_GEMM_WGRAD_KGROUPED = 1 } fp8q_gemm_mode_t;
+
+/* ABI version (FP8Q_ABI_VERSION) and a static text for a status code. */
+int fp8q_abi_version(void);
+const char* fp8q_status_string(fp8q_status_t status);
+
+/* Rowwise quantization of activations (ai-radar.it, introduction and "Il guadagno vero e' nel
+ * movimento dei dati": one scale per token row, chain absmax -> scale -> clamp -> cast, fused
+ * into a single pass over HBM).
+ *   x       bf16 [rows][ld_x], ld_x >= cols
+ *   q       u8   [rows][ld_q], ld_q >= cols: the FP8 bytes of each row
+ *   scales  fp32 [rows]: s[r] = FMAX / max(max_k |x[r,k]|, 1e-12f)
+ * rows == 0 or cols == 0 is a no-op that still validates its arguments (cols == 0 with
+ * rows > 0 writes s = FMAX/1e-12f). */
+fp8q_status_t fp8_quant_rowwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                fp8q_format_t fmt, uint8_t* q, int64_t ld_q, float* scales,
+                                hipStream_t stream);
+
+/* Bytes of device workspace fp8_quant_colwise_grouped needs (its cross-block maxima). */
+size_t fp8_quant_colwise_grouped_workspace_size(int64_t rows, int64_t cols, int32_t groups);
+
+/* Columnwise quantization per row group with a transposed FP8 output (ai-radar.it,
+ * introduction: colwise scales on per-expert weights, token groups from an offset tensor;
+ * "Il guadagno vero e' nel movimento dei dati": the backward's transposed operand written
+ * directly, output tile transposed through LDS, relaxed atomics for cross-block maxima).
+ * For group g (rows [o[g-1], o[g])) and column c:
+ *   scales[g*cols + c] = FMAX / max(max_{r in g} |x[r,c]|, 1e-12f)
+ *   q_t[c*ld_qt + r]   = ENC(clamp(RN32(x[r,c] * scales[g*cols + c])))  for r in g
+ * i.e. q_t is the column-major copy of the whole quantized matrix.  An empty group writes its
+ * scales (FMAX/1e-12f) and no bytes.  Weights [E,K,N] viewed as [E*K, N] with offsets
+ * K, 2K, ... give per-(expert, output column) scales and the K-contiguous B operand [N, E*K]
+ * of the forward grouped GEMM; activations/gradients [M, C] with token offsets give the
+ * per-(group, column) operands of the weight-gradient GEMM.
+ *   x          bf16 [rows][ld_x]
+ *   offsets    int32 [groups] device, groups >= 1
+ *   q_t        u8   [cols][ld_qt], ld_qt >= rows
+ *   scales     fp32 [groups][cols]
+ *   workspace  device, >= fp8_quant_colwise_grouped_workspace_size(rows, cols, groups) bytes,
+ *              no initial content required; its content after the call is unspecified.
+ * Concurrent calls must use distinct workspaces. */
+fp8q_status_t fp8_quant_colwise_grouped(const uint16_t* x, int64_t rows, int64_t cols,
+                                        int64_t ld_x, const int32_t* offsets, int32_t groups,
+                                        fp8q_format_t fmt, uint8_t* q_t, int64_t ld_qt,
+                                        float* scales, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
+
+/* Scaled FP8 grouped GEMM with fp32 accumulation on FP8 MFMA and dequantization fused into
+ * the epilogue; bf16 output, rounded to nearest even (latestnews.news third paragraph: grouped
+ * GEMM for MoE on ROCm; fosswire.org "What Primus adds for MoE training on MI355X": FP8 grouped
+ * GEMM for the expert FFNs).  fmt is the encoding of both operands.
+ *
+ * mode FP8Q_GEMM_FWD_MGROUPED (forward, groups along M):
+ *   a         Xq  u8 [M][lda], lda >= K               a_scales fp32 [M]
+ *   b         per group g the matrix b + g*b_group_stride, rows n = 0..N-1 at stride ldb,
+ *             K bytes each (K-contiguous) ldb >= K    b_scales fp32 [groups][N]
+ *             (weights quantized by fp8_quant_colwise_grouped into [N, E*K]: ldb = E*K,
+ *             b_group_stride = K; weights stored [E,N,K]: ldb = K, b_group_stride = N*K)
+ *   c         bf16 [M][ldc], ldc >= N
+ *   c[m,n] = bf16( (sum_k dec(a[m,k]) * dec(b_g[n,k])) * (1/a_scales[m]) * (1/b_scales[g,n]) )
+ *   for m in group g.
+ * mode FP8Q_GEMM_WGRAD_KGROUPED (weight gradient, groups along the contraction dimension):
+ *   a         XqT u8 [K][lda], lda >= M (column-major quantized activations)
+ *   a_scales  fp32 [groups][K]
+ *   b         dYqT u8 [N][ldb], ldb >= M              b_scales fp32 [groups][N]
+ *   b_group_stride must be 0
+ *   c         bf16 [groups][K][ldc], ldc >= N, group stride K*ldc
+ *   c[g,k,n] = bf16( (sum_{m in g} dec(a[k,m]) * dec(b[n,m])) / (a_scales[g,k]*b_scales[g,n]) )
+ *   An empty group writes zeros.
+ * Accumulation is fp32 on the matrix cores; the result is within 1e-3 + 1e-2*|exact| of the
+ * exactly accumulated value for the sizes this library targets.  Element bits of c are not
+ * specified beyond that bound. */
+fp8q_status_t fp8_grouped_gemm(fp8q_gemm_mode_t mode, fp8q_format_t fmt, const uint8_t* a,
+                               int64_t lda, const float* a_scales, const uint8_t* b,
+                               int64_t ldb, int64_t b_group_stride, const float* b_scales,
+                               const int32_t* offsets, int32_t groups, int64_t M, int64_t N,
+                               int64_t K, uint16_t* c, int64_t ldc, hipStream_t stream);
+
+/* MXFP8 quantization along rows (OCP MX v1.0; the pages only name MXFP8 kernels for MI355X in
+ * "What Primus adds for MoE training on MI355X"): blocks of 32 consecutive elements of a row
+ * share one E8M0 scale byte.  For each block: a = max |x|; e = floor(log2 a) - 8 (8 is the
+ * exponent of e4m3fn's largest value), clamped to [-127, 127], e = -127 for an all-zero block;
+ * e8m0 byte = e + 127; q = ENC_e4m3fn(clamp(x * 2^-e, -448, 448)).  Elements are OCP e4m3fn.
+ *   x       bf16 [rows][ld_x], cols % 32 == 0
+ *   q       u8   [rows][ld_q]
+ *   e8m0    u8   [rows][ld_s], ld_s >= cols/32 */
+fp8q_status_t fp8_mx_quant_rowwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                   uint8_t* q, int64_t ld_q, uint8_t* e8m0, int64_t ld_s,
+                                   hipStream_t stream);
+
+/* MXFP8 quantization along columns with a transposed output: blocks of 32 consecutive rows of
+ * one column share a scale.  Same per-block rule as fp8_mx_quant_rowwise.  Used for weights
+ * [E*K, N] (K % 32 == 0) to obtain the K-contiguous B operand [N, E*K] and its scales.
+ *   x       bf16 [rows][ld_x], rows % 32 == 0
+ *   q_t     u8   [cols][ld_qt], ld_qt >= rows: q_t[c*ld_qt + r]
+ *   e8m0    u8   [cols][ld_s], ld_s >= rows/32: e8m0[c*ld_s + r/32] */
+fp8q_status_t fp8_mx_quant_colwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                   uint8_t* q_t, int64_t ld_qt, uint8_t* e8m0, int64_t ld_s,
+                                   hipStream_t stream);
+
+/* MXFP8 grouped GEMM, forward (groups along M), on gfx950's block-scaled FP8 MFMA:
+ *   c[m,n] = bf16( sum_kb 2^(ea[m,kb] + eb_g[n,kb]) * sum_{k in kb} dec(a[m,k]) * dec(b_g[n,k]) )
+ * with ea = a_e8m0[m*ld_sa + kb] - 127, eb_g = b_e8m0[g*sb_group_stride + n*ld_sb + kb] - 127,
+ * b_g = b + g*b_group_stride (rows n at stride ldb), K % 32 == 0, e4m3fn elements, fp32
+ * accumulation.  Weights from fp8_mx_quant_colwise on [E*K, N]: ldb = E*K,
+ * b_group_stride = K, ld_sb = E*K/32, sb_group_stride = K/32. */
+fp8q_status_t fp8_mx_grouped_gemm(const uint8_t* a, int64_t lda, const uint8_t* a_e8m0,
+                                  int64_t ld_sa, const uint8_t* b, int64_t ldb,
+                                  int64_t b_group_stride, const uint8_t* b_e8m0, int64_t ld_sb,
+                                  int64_t sb_group_stride, const int32_t* offsets,
+                                  int32_t groups, int64_t M, int64_t N, int64_t K, uint16_t* c,
+                                  int64_t ldc, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8_QUANT_GROUPED_H */

@@ -1,0 +1,87 @@
+"""The C-ABI library (CPU only: no compute calls).
+
+The built library must load and export every function the public header declares, with no
+torch types in the signatures; the Python binding must declare a matching signature for each.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8_quant_grouped.h")
+LIB = os.path.join(ROOT, "fp8_quantization_grouped_amd", "libfp8qg.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z0-9_]+)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_hot_path():
+    names = declared_functions()
+    for must in ("fp8_quant_rowwise", "fp8_quant_colwise_grouped", "fp8_grouped_gemm",
+                 "fp8_mx_quant_rowwise", "fp8_mx_quant_colwise", "fp8_mx_grouped_gemm",
+                 "fp8_quant_colwise_grouped_workspace_size", "fp8q_status_string",
+                 "fp8q_abi_version"):
+        assert must in names
+    text = open(HEADER).read()
+    assert "torch" not in re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} not built (run __graft_entry__.build())")
+    return ctypes.CDLL(LIB)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_covers_every_symbol():
+    import fp8_quantization_grouped_amd as fq
+    assert sorted(fq.SIGNATURES) == declared_functions()
+
+
+def test_host_only_calls(lib):
+    lib.fp8q_abi_version.restype = ctypes.c_int
+    assert lib.fp8q_abi_version() == 1
+    lib.fp8q_status_string.restype = ctypes.c_char_p
+    lib.fp8q_status_string.argtypes = [ctypes.c_int]
+    assert lib.fp8q_status_string(0) == b"ok"
+    assert lib.fp8q_status_string(3) == b"workspace too small"
+    f = lib.fp8_quant_colwise_grouped_workspace_size
+    f.restype = ctypes.c_size_t
+    f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
+    assert f(16384, 7168, 32) == 32 * 7168 * 4
+    assert f(10, 3, 1) == 256
+    assert f(10, -1, 1) == 0
+
+
+def test_argument_errors_are_caught_on_the_host(lib):
+    """Invalid arguments return a status before any device work (no GPU needed)."""
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    f = lib.fp8_quant_rowwise
+    f.restype = I
+    f.argtypes = [P, I64, I64, I64, I, P, I64, P, P]
+    dummy = ctypes.c_void_p(16)  # never dereferenced: every call below fails validation
+    assert f(dummy, -1, 8, 8, 1, dummy, 8, dummy, None) == 1
+    assert f(dummy, 4, 8, 4, 1, dummy, 8, dummy, None) == 1
+    assert f(dummy, 4, 8, 8, 2, dummy, 8, dummy, None) == 1
+    assert f(dummy, 0, 8, 8, 1, dummy, 8, dummy, None) == 0  # empty: no-op
+    g = lib.fp8_grouped_gemm
+    g.restype = I
+    g.argtypes = [I, I, P, I64, P, P, I64, I64, P, P, ctypes.c_int32, I64, I64, I64, P, I64, P]
+    assert g(5, 1, dummy, 16, dummy, dummy, 16, 0, dummy, dummy, 1, 4, 4, 16, dummy, 4, None) == 1
+    assert g(0, 1, dummy, 16, dummy, dummy, 16, 0, dummy, dummy, 0, 4, 4, 16, dummy, 4, None) == 1
+    assert g(1, 1, dummy, 16, dummy, dummy, 16, 16, dummy, dummy, 1, 4, 4, 16, dummy, 4,
+             None) == 1  # wgrad needs b_group_stride == 0

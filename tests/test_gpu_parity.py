@@ -1,0 +1,358 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on the same seeded
+inputs.  Quantized bytes and scales must match bit for bit; GEMM outputs must lie within
+1e-3 + 1e-2*|exact| of the oracle's exactly accumulated result (the oracle value is the exact
+sum scaled by 1/(sa*sb), before output rounding).
+
+Sizes are small enough for the oracle to finish in seconds while spanning several tiles of
+every kernel (256x64 quant tiles, 128x128 GEMM tiles, 128-byte contraction steps) with ragged
+tails, empty groups and groups that start or end on tile boundaries.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests import pinlib
+
+pytestmark = pytest.mark.gpu
+
+FNUZ, FN = 0, 1
+FMTS = [FNUZ, FN]
+
+
+@pytest.fixture(scope="module")
+def fq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fp8_quantization_grouped_amd as m
+    m.lib()  # raises if the HIP library is missing
+    return m
+
+
+DEV = "cuda:0"
+
+
+def dev_bf16(bits, ld=None):
+    return workloads.to_torch_bf16(bits, DEV, ld)
+
+
+def dev_i32(a):
+    return torch.tensor(np.asarray(a, dtype=np.int32), device=DEV)
+
+
+def gemm_tol_check(got, ref, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    excess = np.abs(got - ref) - (1e-3 + 1e-2 * np.abs(ref))
+    i = int(np.argmax(excess))
+    assert excess.flat[i] <= 0, (f"{what}: |err| {abs(got.flat[i] - ref.flat[i]):.4g} at flat "
+                                 f"{i} (gpu {got.flat[i]:.6g}, oracle {ref.flat[i]:.6g})")
+
+
+# ----------------------------------------------------------------------------- codec / scale
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_scale_exhaustive_over_bf16_amax(fq, fmt):
+    """Every positive finite bf16 value as a row absmax: the GPU's IEEE division must give the
+    oracle's fp32 scale bit for bit."""
+    bits = np.arange(0x0001, 0x7F80, dtype=np.uint16)
+    x = np.zeros((bits.size, 8), np.uint16)
+    x[:, 3] = bits
+    x[1::2, 3] |= np.uint16(0x8000)  # the sign must not matter
+    q, s = fq.fp8_quant_rowwise(dev_bf16(x), fmt)
+    oq, os_ = oracle.quant_rowwise(x, fmt)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), oq)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("amax_bits", [0x3F80, 0x4040, 0x3F33, 0x3A83, 0x4348, 0x7149, 0x0F00])
+def test_rowwise_every_bf16_value(fq, fmt, amax_bits):
+    """A row holding every finite bf16 value with |x| <= amax (plus the amax itself): the
+    hardware conversion path must reproduce the oracle's encoding of every product."""
+    allb = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    f = workloads.bf16_bits_to_f32(allb)
+    amax = float(workloads.bf16_bits_to_f32(np.array([amax_bits], np.uint16))[0])
+    vals = allb[np.isfinite(f) & (np.abs(f) <= amax)]
+    row = np.concatenate([vals, np.array([amax_bits], np.uint16)])
+    pad = (-row.size) % 8
+    row = np.concatenate([row, np.zeros(pad, np.uint16)])
+    # split the values over many rows of the same amax so several kernels shapes are used
+    nrow = 16
+    per = -(-row.size // nrow)
+    per += (-per) % 8
+    x = np.zeros((nrow, per), np.uint16)
+    flat = x.reshape(-1)
+    flat[:row.size] = row
+    x[:, -1] = amax_bits  # every row has the same absmax
+    q, s = fq.fp8_quant_rowwise(dev_bf16(x), fmt)
+    oq, os_ = oracle.quant_rowwise(x, fmt)
+    assert np.array_equal(s.cpu().numpy(), os_)
+    gq = q.cpu().numpy()
+    bad = np.argwhere(gq != oq)
+    assert bad.size == 0, [(int(x[r, c]), hex(gq[r, c]), hex(oq[r, c])) for r, c in bad[:8]]
+
+
+# ----------------------------------------------------------------------------- rowwise
+
+ROW_SHAPES = [(1, 8), (5, 24), (33, 256), (100, 520), (64, 1000), (17, 4096), (9, 8200),
+              (3, 20000), (2, 40000), (7, 13)]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", ROW_SHAPES)
+def test_rowwise_parity(fq, fmt, shape):
+    rows, cols = shape
+    x = workloads.make_matrix(100 + rows, rows, cols, 1.0, 0.01)
+    x[0, :] = 0  # an all-zero row
+    q, s = fq.fp8_quant_rowwise(dev_bf16(x), fmt)
+    oq, os_ = oracle.quant_rowwise(x, fmt)
+    assert np.array_equal(s.cpu().numpy(), os_)
+    assert np.array_equal(q.cpu().numpy(), oq)
+    if fmt == FNUZ:
+        assert not np.any(q.cpu().numpy() == 0x80)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_rowwise_padded_leading_dims(fq, fmt):
+    rows, cols = 37, 384
+    x = workloads.make_matrix(7, rows, cols, 3.0, 0.02)
+    xd = dev_bf16(x, ld=cols + 64)
+    qbuf = torch.full((rows, cols + 32), 0xAB, dtype=torch.uint8, device=DEV)
+    q, s = fq.fp8_quant_rowwise(xd, fmt, q=qbuf[:, :cols])
+    oq, os_ = oracle.quant_rowwise(x, fmt)
+    qb = qbuf.cpu().numpy()
+    assert np.array_equal(qb[:, :cols], oq) and np.array_equal(s.cpu().numpy(), os_)
+    assert np.all(qb[:, cols:] == 0xAB)  # nothing written past the row
+
+
+# ----------------------------------------------------------------------------- colwise
+
+COL_CASES = [
+    # rows, cols, offsets
+    (300, 72, [300]),
+    (513, 130, [0, 37, 37, 256, 256, 257, 512, 513]),
+    (700, 64, [100, 100, 356, 612, 700, 700]),
+    (1024, 200, [444, 509, 893, 1024]),
+    (96, 40, [10, 20, 30, 40, 50, 60, 70, 80, 90, 91, 92, 96]),
+    (1, 8, [1]),
+    (259, 21, [3, 259]),          # columns not a multiple of 8 -> element-wise path
+]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("case", COL_CASES)
+def test_colwise_grouped_parity(fq, fmt, case):
+    rows, cols, off = case
+    x = workloads.make_matrix(200 + rows + cols, rows, cols, 1.0, 0.01)
+    off = np.asarray(off, np.int32)
+    qt, s = fq.fp8_quant_colwise_grouped(dev_bf16(x), dev_i32(off), fmt)
+    oqt, os_ = oracle.quant_colwise_grouped(x, off, fmt)
+    assert np.array_equal(s.cpu().numpy(), os_)
+    assert np.array_equal(qt.cpu().numpy(), oqt)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_colwise_unaligned_output_stride(fq, fmt):
+    rows, cols = 300, 64
+    x = workloads.make_matrix(5, rows, cols)
+    off = np.array([120, 300], np.int32)
+    buf = torch.full((cols, rows + 5), 0xCD, dtype=torch.uint8, device=DEV)
+    qt, s = fq.fp8_quant_colwise_grouped(dev_bf16(x, ld=cols + 8), dev_i32(off), fmt,
+                                         q_t=buf[:, :rows])
+    oqt, os_ = oracle.quant_colwise_grouped(x, off, fmt)
+    b = buf.cpu().numpy()
+    assert np.array_equal(b[:, :rows], oqt) and np.array_equal(s.cpu().numpy(), os_)
+    assert np.all(b[:, rows:] == 0xCD)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_colwise_zero_rows_writes_empty_scales(fq, fmt):
+    x = torch.zeros((0, 16), dtype=torch.bfloat16, device=DEV)
+    off = dev_i32([0, 0, 0])
+    qt, s = fq.fp8_quant_colwise_grouped(x, off, fmt)
+    want = np.float32(pinlib.FMAX[fmt]) / np.float32(1e-12)
+    assert np.all(s.cpu().numpy() == want)
+
+
+def test_colwise_deterministic_across_calls(fq):
+    """Relaxed atomics combine maxima in any order; max is exact, so repeated calls (with the
+    workspace reused and not cleared by the caller) give identical bytes."""
+    x = workloads.make_matrix(9, 1500, 136, 1.0, 0.01)
+    off = dev_i32([200, 700, 701, 1500])
+    ws = torch.empty(fq.fp8_quant_colwise_grouped_workspace_size(1500, 136, 4) + 256,
+                     dtype=torch.uint8, device=DEV)
+    ref = None
+    for _ in range(5):
+        qt, s = fq.fp8_quant_colwise_grouped(dev_bf16(x), off, FN, workspace=ws)
+        cur = (qt.cpu().numpy(), s.cpu().numpy())
+        if ref is None:
+            ref = cur
+        assert np.array_equal(cur[0], ref[0]) and np.array_equal(cur[1], ref[1])
+
+
+# ----------------------------------------------------------------------------- grouped GEMM
+
+def _fwd_operands(fmt, M, K, N, E, seed):
+    x = workloads.make_matrix(seed, M, K, 1.0, 0.01)
+    w = workloads.make_matrix(seed + 1, E * K, N, 0.02)
+    qa, sa = oracle.quant_rowwise(x, fmt)
+    qbt, sb = oracle.quant_colwise_grouped(w, (np.arange(1, E + 1) * K).astype(np.int32), fmt)
+    return qa, sa, qbt, sb
+
+
+GEMM_FWD_CASES = [
+    # M, K, N, offsets
+    (1024, 256, 512, [444, 509, 893, 1024]),
+    (300, 144, 200, [0, 1, 129, 129, 300]),
+    (64, 128, 16, [64]),
+    (515, 512, 130, [128, 128, 256, 300, 515]),
+]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("case", GEMM_FWD_CASES)
+def test_gemm_fwd_parity(fq, fmt, case):
+    M, K, N, off = case
+    off = np.asarray(off, np.int32)
+    E = off.size
+    qa, sa, qbt, sb = _fwd_operands(fmt, M, K, N, E, 300 + M)
+    c = fq.fp8_grouped_gemm(fq.GEMM_FWD_MGROUPED, fmt, torch.from_numpy(qa).to(DEV),
+                            torch.from_numpy(sa).to(DEV), torch.from_numpy(qbt).to(DEV),
+                            torch.from_numpy(sb).to(DEV), dev_i32(off), M, N, K,
+                            ldb=E * K, b_group_stride=K)
+    got = c.float().cpu().numpy()
+    ref = oracle.gemm_fwd_rows(fmt, qa, sa, qbt, E * K, K, sb, off, N, K, np.arange(M))
+    gemm_tol_check(got, ref, f"fwd {case}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemm_fwd_expert_major_weights(fq, fmt):
+    """Weights stored [E, N, K] (b_group_stride = N*K, ldb = K), quantized rowwise along K."""
+    M, K, N, E = 400, 256, 96, 3
+    off = np.array([150, 150, 400], np.int32)
+    x = workloads.make_matrix(41, M, K, 1.0, 0.01)
+    w = workloads.make_matrix(42, E * N, K, 0.02)  # [E*N, K]
+    qa, sa = oracle.quant_rowwise(x, fmt)
+    qb, sbf = oracle.quant_rowwise(w, fmt)        # per (e, n) scale over K
+    c = fq.fp8_grouped_gemm(fq.GEMM_FWD_MGROUPED, fmt, torch.from_numpy(qa).to(DEV),
+                            torch.from_numpy(sa).to(DEV), torch.from_numpy(qb).to(DEV),
+                            torch.from_numpy(sbf).to(DEV), dev_i32(off), M, N, K, ldb=K,
+                            b_group_stride=N * K)
+    ref = oracle.gemm_fwd_rows(fmt, qa, sa, qb, K, N * K, sbf, off, N, K, np.arange(M))
+    gemm_tol_check(c.float().cpu().numpy(), ref, "fwd expert-major")
+
+
+GEMM_WGRAD_CASES = [
+    # M (tokens), K, N, offsets
+    (1000, 160, 96, [100, 100, 357, 358, 1000]),
+    (300, 128, 128, [300]),
+    (777, 200, 72, [16, 32, 300, 301, 700, 777, 777]),
+]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("case", GEMM_WGRAD_CASES)
+def test_gemm_wgrad_parity(fq, fmt, case):
+    M, K, N, off = case
+    off = np.asarray(off, np.int32)
+    G = off.size
+    x = workloads.make_matrix(500 + M, M, K)
+    dy = workloads.make_matrix(600 + M, M, N)
+    xt, sx = oracle.quant_colwise_grouped(x, off, fmt)    # [K, M], [G, K]
+    dyt, sdy = oracle.quant_colwise_grouped(dy, off, fmt)  # [N, M], [G, N]
+    # the weight-gradient operands need 16-byte aligned rows: pad the token dimension
+    ldp = -(-M // 16) * 16
+
+    def padded(a):
+        t = torch.zeros((a.shape[0], ldp), dtype=torch.uint8, device=DEV)
+        t[:, :M] = torch.from_numpy(a).to(DEV)
+        return t
+
+    c = fq.fp8_grouped_gemm(fq.GEMM_WGRAD_KGROUPED, fmt, padded(xt),
+                            torch.from_numpy(sx).to(DEV), padded(dyt),
+                            torch.from_numpy(sdy).to(DEV), dev_i32(off), M, N, K, ldb=ldp)
+    got = c.float().cpu().numpy()
+    gi = np.repeat(np.arange(G, dtype=np.int32), K)
+    ki = np.tile(np.arange(K, dtype=np.int64), G)
+    ref = oracle.gemm_wgrad_rows(fmt, xt, sx, dyt, sdy, off, N, K, gi, ki).reshape(G, K, N)
+    gemm_tol_check(got, ref, f"wgrad {case}")
+    start = 0
+    for g, end in enumerate(off):
+        if end == start:
+            assert np.all(got[g] == 0)
+        start = end
+
+
+# ----------------------------------------------------------------------------- MXFP8
+
+@pytest.mark.parametrize("shape", [(3, 32), (40, 1024), (17, 7168), (5, 2080)])
+def test_mx_rowwise_parity(fq, shape):
+    rows, cols = shape
+    x = workloads.make_matrix(700 + cols, rows, cols, 1.0, 0.02)
+    x[0, :32] = 0
+    q, e8 = fq.fp8_mx_quant_rowwise(dev_bf16(x))
+    oq, oe = oracle.mx_quant_rowwise(x)
+    assert np.array_equal(e8.cpu().numpy(), oe)
+    assert np.array_equal(q.cpu().numpy(), oq)
+
+
+def test_mx_rowwise_every_exponent(fq):
+    bits = np.arange(0x0001, 0x7F80, dtype=np.uint16)
+    n = bits.size - bits.size % 4
+    x = np.zeros((n // 4, 4 * 32), np.uint16)
+    x.reshape(-1, 32)[:, 7] = bits[:n]
+    x.reshape(-1, 32)[:, 9] = bits[:n] ^ np.uint16(0x8000)
+    q, e8 = fq.fp8_mx_quant_rowwise(dev_bf16(x))
+    oq, oe = oracle.mx_quant_rowwise(x)
+    assert np.array_equal(e8.cpu().numpy(), oe) and np.array_equal(q.cpu().numpy(), oq)
+
+
+@pytest.mark.parametrize("shape", [(32, 8), (256, 64), (544, 136), (96, 40)])
+def test_mx_colwise_parity(fq, shape):
+    rows, cols = shape
+    x = workloads.make_matrix(800 + rows, rows, cols, 0.02, 0.01)
+    qt, e8 = fq.fp8_mx_quant_colwise(dev_bf16(x))
+    oqt, oe = oracle.mx_quant_colwise(x)
+    assert np.array_equal(e8.cpu().numpy(), oe)
+    assert np.array_equal(qt.cpu().numpy(), oqt)
+
+
+@pytest.mark.parametrize("case", [(300, 256, 96, [100, 100, 300]),
+                                  (515, 512, 130, [128, 256, 300, 515]),
+                                  (64, 160, 64, [64])])
+def test_mx_gemm_parity(fq, case):
+    M, K, N, off = case
+    off = np.asarray(off, np.int32)
+    E = off.size
+    x = workloads.make_matrix(900 + M, M, K, 1.0, 0.01)
+    w = workloads.make_matrix(901 + M, E * K, N, 0.02)
+    qa, ea = oracle.mx_quant_rowwise(x)
+    qbt, eb = oracle.mx_quant_colwise(w)  # [N, E*K], [N, E*K/32]
+    c = fq.fp8_mx_grouped_gemm(torch.from_numpy(qa).to(DEV), torch.from_numpy(ea).to(DEV),
+                               torch.from_numpy(qbt).to(DEV), torch.from_numpy(eb).to(DEV),
+                               dev_i32(off), M, N, K, ldb=E * K, b_group_stride=K,
+                               ld_sb=E * K // 32, sb_group_stride=K // 32)
+    ref = oracle.mx_gemm_fwd_rows(qa, ea, qbt, E * K, K, eb, E * K // 32, K // 32, off, N, K,
+                                  np.arange(M))
+    gemm_tol_check(c.float().cpu().numpy(), ref, f"mx {case}")
+
+
+# ----------------------------------------------------------------------------- argument errors
+
+def test_invalid_arguments_return_status(fq):
+    L = fq.lib()
+    x = torch.zeros((4, 8), dtype=torch.bfloat16, device=DEV)
+    q = torch.zeros((4, 8), dtype=torch.uint8, device=DEV)
+    s = torch.zeros((4,), dtype=torch.float32, device=DEV)
+    p = lambda t: t.data_ptr()
+    assert L.fp8_quant_rowwise(p(x), 4, 8, 4, 1, p(q), 8, p(s), None) == 1   # ld_x < cols
+    assert L.fp8_quant_rowwise(p(x), 4, 8, 8, 7, p(q), 8, p(s), None) == 1   # bad format
+    assert L.fp8_quant_rowwise(None, 4, 8, 8, 1, p(q), 8, p(s), None) == 1   # null input
+    off = dev_i32([4])
+    assert L.fp8_quant_colwise_grouped(p(x), 4, 8, 8, p(off), 1, 1, p(q), 4, p(s), p(q), 4,
+                                       None) == 3  # workspace too small
+    assert L.fp8_grouped_gemm(0, 1, p(q), 8, p(s), p(q), 8, 0, p(s), p(off), 1, 4, 4, 8, p(x),
+                              4, None) == 2  # K not a multiple of 16

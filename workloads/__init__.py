@@ -167,3 +167,15 @@ def make_matrix(seed: int, rows: int, cols: int, std: float = 1.0, outlier_frac:
         mask = rng.random((rows, cols)) < outlier_frac
         x[mask] *= np.float32(outlier_mul)
     return f32_to_bf16_bits(x)
+
+
+def to_torch_bf16(bits: np.ndarray, device, ld: int | None = None):
+    """Copy bf16 bit patterns to a device bf16 tensor (optionally with a padded row stride)."""
+    import torch
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    if ld is None or bits.ndim != 2 or ld == bits.shape[1]:
+        return t.to(device)
+    out = torch.zeros((bits.shape[0], ld), dtype=torch.bfloat16, device=device)
+    out[:, :bits.shape[1]] = t.to(device)
+    return out[:, :bits.shape[1]]
