@@ -1,0 +1,300 @@
+"""Benchmark of the MoE FP8 training hot path on one MI355X.
+
+One step = one pass of every hot-path operation over one batch of synthetic input resident in
+HBM:
+  forward   rowwise quant of X, per-expert colwise quant of W (transposed), M-grouped FP8 GEMM
+  backward  colwise-grouped transposed quant of X and dY, K-grouped FP8 weight-gradient GEMM
+  MXFP8     MX rowwise quant of X, MX colwise quant of W, MX grouped GEMM (forward)
+Default workload: the DeepSeek-V3-shaped local expert slice (32 experts, hidden 7168,
+intermediate 2048, 16384 routed token rows, Zipf(1.1) group sizes), e4m3fn.
+
+Timing: W untimed warm-up steps, then exactly K timed steps between device synchronisations;
+every operation is also bracketed with HIP events on the stream it runs on, giving per-launch
+averages.  The JSON line reports whole-step throughput (algorithmic GEMM flops of the step per
+second of step time, quantization time included), the quantizers' aggregate GB/s, the GEMMs'
+TFLOP/s, a roofline entry for the kernel that takes the most time, and the CPU oracle timed on a
+bounded sample on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "quantize GB/s (% HBM peak) + FP8 grouped GEMM TFLOP/s (% MFMA peak)"
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense FP8 (and MXFP8) matrix throughput
+
+WORKLOADS = {
+    # name: (workloads-module config, format, ops)
+    "dsv3": ("dsv3_bwd", 1, ("fwd", "wgrad", "mx")),
+    "dense": ("dense", 1, ("fwd",)),
+    "moe16b": ("moe16b", 1, ("fwd",)),
+    "tiny": ("tiny", 0, ("fwd", "wgrad")),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def make_inputs(name, torch, dev):
+    """Device-resident synthetic inputs.  Group offsets come from the seeded numpy recipe of the
+    workloads module; the bf16 tensors are drawn on the device with a seeded generator (same
+    distributions as the recipe: X, dY ~ N(0,1), W ~ N(0, 0.02); the tiny workload adds 1% x50
+    outliers)."""
+    import workloads
+    cfg_name, fmt, ops = WORKLOADS[name]
+    cfg = workloads.CONFIGS[cfg_name]
+    M, K, N, E = cfg["M"], cfg["K"], cfg["N"], cfg["E"]
+    rng = np.random.Generator(np.random.PCG64(cfg["seed"]))
+    if cfg_name == "dense":
+        offsets = np.array([M], np.int32)
+    elif cfg_name == "moe16b":
+        offsets = workloads.routed_offsets_topk(rng, cfg["tokens"], E, cfg["topk"])
+    elif cfg_name == "tiny":
+        offsets = workloads.random_offsets(rng, M, E)
+    else:
+        offsets = workloads.multinomial_offsets(rng, M, E)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(int(cfg["seed"]))
+    x = torch.randn((M, K), generator=gen, device=dev, dtype=torch.float32)
+    if cfg_name == "tiny":
+        mask = torch.rand((M, K), generator=gen, device=dev) < 0.01
+        x = torch.where(mask, x * 50.0, x)
+    x = x.to(torch.bfloat16)
+    w = (torch.randn((E * K, N), generator=gen, device=dev, dtype=torch.float32) * 0.02).to(
+        torch.bfloat16)
+    dy = None
+    if "wgrad" in ops:
+        dy = torch.randn((M, N), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    return dict(M=M, K=K, N=N, E=E, fmt=fmt, ops=ops, x=x, w=w, dy=dy,
+                offsets=torch.tensor(offsets, dtype=torch.int32, device=dev),
+                offsets_np=offsets, cfg_name=cfg_name)
+
+
+class Step:
+    """Pre-allocated outputs/workspaces and the per-operation launch sequence."""
+
+    def __init__(self, fq, torch, d):
+        self.fq, self.torch, self.d = fq, torch, d
+        dev = d["x"].device
+        M, K, N, E = d["M"], d["K"], d["N"], d["E"]
+        u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+        e = lambda *s, dt=u8: torch.empty(s, dtype=dt, device=dev)
+        self.off_w = torch.tensor(np.arange(1, E + 1, dtype=np.int32) * K, device=dev)
+        G = d["offsets"].numel()
+        ldm = -(-M // 16) * 16  # 16-byte aligned token rows for the transposed operands
+        self.buf = dict(
+            xq=e(M, K), sx=e(M, dt=f32), wqt=e(N, E * K), sw=e(E, N, dt=f32), y=e(M, N, dt=bf),
+            ws_w=e(max(256, fq.fp8_quant_colwise_grouped_workspace_size(E * K, N, E))),
+        )
+        if "wgrad" in d["ops"]:
+            self.buf.update(
+                xqt=e(K, ldm), sxg=e(G, K, dt=f32), dyqt=e(N, ldm), sdyg=e(G, N, dt=f32),
+                dw=e(G, K, N, dt=bf),
+                ws_x=e(max(256, fq.fp8_quant_colwise_grouped_workspace_size(M, K, G))),
+                ws_dy=e(max(256, fq.fp8_quant_colwise_grouped_workspace_size(M, N, G))))
+        if "mx" in d["ops"]:
+            self.buf.update(mxq=e(M, K), mxe=e(M, K // 32), mxwt=e(N, E * K),
+                            mxwe=e(N, E * K // 32), ymx=e(M, N, dt=bf))
+        self.ldm = ldm
+        self.flops = {}
+        self.bytes = {}
+        self.units = {}
+        tot_m = M
+        self.flops["gemm_fwd"] = 2.0 * tot_m * N * K
+        self.bytes["quant_rowwise_x"] = M * K * 3 + M * 4
+        self.bytes["quant_colwise_w"] = E * K * N * 3 + E * N * 4
+        if "wgrad" in d["ops"]:
+            self.flops["gemm_wgrad"] = 2.0 * M * N * K
+            self.bytes["quant_colwise_xT"] = M * K * 3 + G * K * 4
+            self.bytes["quant_colwise_dyT"] = M * N * 3 + G * N * 4
+        if "mx" in d["ops"]:
+            self.flops["gemm_mx"] = 2.0 * M * N * K
+            self.bytes["mx_quant_rowwise_x"] = M * K * 3 + M * K // 32
+            self.bytes["mx_quant_colwise_w"] = E * K * N * 3 + E * K * N // 32
+
+    def ops(self):
+        fq, d, b = self.fq, self.d, self.buf
+        M, K, N, E, fmt = d["M"], d["K"], d["N"], d["E"], d["fmt"]
+        seq = [
+            ("quant_rowwise_x", lambda: fq.fp8_quant_rowwise(d["x"], fmt, q=b["xq"],
+                                                             scales=b["sx"])),
+            ("quant_colwise_w", lambda: fq.fp8_quant_colwise_grouped(
+                d["w"], self.off_w, fmt, q_t=b["wqt"], scales=b["sw"].view(E, N),
+                workspace=b["ws_w"])),
+            ("gemm_fwd", lambda: fq.fp8_grouped_gemm(
+                fq.GEMM_FWD_MGROUPED, fmt, b["xq"], b["sx"], b["wqt"], b["sw"], d["offsets"],
+                M, N, K, ldb=E * K, b_group_stride=K, c=b["y"])),
+        ]
+        if "wgrad" in d["ops"]:
+            seq += [
+                ("quant_colwise_xT", lambda: fq.fp8_quant_colwise_grouped(
+                    d["x"], d["offsets"], fmt, q_t=b["xqt"][:, :M], scales=b["sxg"],
+                    workspace=b["ws_x"])),
+                ("quant_colwise_dyT", lambda: fq.fp8_quant_colwise_grouped(
+                    d["dy"], d["offsets"], fmt, q_t=b["dyqt"][:, :M], scales=b["sdyg"],
+                    workspace=b["ws_dy"])),
+                ("gemm_wgrad", lambda: fq.fp8_grouped_gemm(
+                    fq.GEMM_WGRAD_KGROUPED, fmt, b["xqt"], b["sxg"], b["dyqt"], b["sdyg"],
+                    d["offsets"], M, N, K, ldb=self.ldm, c=b["dw"])),
+            ]
+        if "mx" in d["ops"]:
+            seq += [
+                ("mx_quant_rowwise_x", lambda: fq.fp8_mx_quant_rowwise(d["x"], q=b["mxq"],
+                                                                      e8m0=b["mxe"])),
+                ("mx_quant_colwise_w", lambda: fq.fp8_mx_quant_colwise(d["w"], q_t=b["mxwt"],
+                                                                      e8m0=b["mxwe"])),
+                ("gemm_mx", lambda: fq.fp8_mx_grouped_gemm(
+                    b["mxq"], b["mxe"], b["mxwt"], b["mxwe"], d["offsets"], M, N, K,
+                    ldb=E * K, b_group_stride=K, ld_sb=E * K // 32, sb_group_stride=K // 32,
+                    c=b["ymx"])),
+            ]
+        return seq
+
+
+def cpu_baseline(d, seconds):
+    """The oracle (never tuned) on the host: forward grouped GEMM rows of the same shapes,
+    on a row sample sized to roughly `seconds` of work, plus rowwise quant GB/s."""
+    import oracle
+    import workloads
+    K, N, fmt = d["K"], d["N"], d["fmt"]
+    rng_seed = 1234
+    xs = workloads.make_matrix(rng_seed, 256, K, 1.0, 0.0)
+    ws = workloads.make_matrix(rng_seed + 1, K, N, 0.02)
+    t0 = time.perf_counter()
+    qa, sa = oracle.quant_rowwise(xs, fmt)
+    tq = time.perf_counter() - t0
+    qbt, sb = oracle.quant_colwise_grouped(ws, np.array([K], np.int32), fmt)
+    off = np.array([qa.shape[0]], np.int32)
+    # calibrate on 4 rows, then run a sample sized to the time budget
+    t0 = time.perf_counter()
+    oracle.gemm_fwd_rows(fmt, qa, sa, qbt, K, 0, sb, off, N, K, np.arange(4))
+    t4 = time.perf_counter() - t0
+    nrows = int(max(4, min(256, 4 * seconds / max(t4, 1e-6))))
+    t0 = time.perf_counter()
+    oracle.gemm_fwd_rows(fmt, qa, sa, qbt, K, 0, sb, off, N, K, np.arange(nrows))
+    tg = time.perf_counter() - t0
+    return dict(value=2.0 * nrows * N * K / tg / 1e12, unit="TFLOP/s", cores=oracle.num_threads(),
+                kind="oracle",
+                sample=(f"forward grouped GEMM, {nrows} rows x N={N} x K={K} ({tg:.1f} s); "
+                        f"rowwise quant of 256x{K} bf16 at {256 * K * 3 / tq / 1e9:.3f} GB/s"),
+                quant_GBps=256 * K * 3 / tq / 1e9)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): this path has no "
+              "multi-GPU mode; expert-parallel sharding is described in DESIGN.md.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import fp8_quantization_grouped_amd as fq
+    fq.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = make_inputs(args.workload, torch, dev)
+    st = Step(fq, torch, d)
+    seq = st.ops()
+    for _ in range(args.warmup):
+        for _, fn in seq:
+            fn()
+    torch.cuda.synchronize()
+    evs = {name: [] for name, _ in seq}
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record()
+    for _ in range(args.steps):
+        for name, fn in seq:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            evs[name].append((a, b))
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    per_op = {n: float(np.mean([a.elapsed_time(b) for a, b in v])) for n, v in evs.items()}
+
+    kernels = {}
+    for n, ms in per_op.items():
+        ent = {"us": round(ms * 1e3, 2)}
+        if n in st.flops:
+            tf = st.flops[n] / (ms * 1e-3) / 1e12
+            ent.update(TFLOPs=round(tf, 1), frac_mfma_peak=round(tf / FP8_PEAK_TFLOPS, 4))
+        if n in st.bytes:
+            gb = st.bytes[n] / (ms * 1e-3) / 1e9
+            ent.update(GBps=round(gb, 1), frac_hbm_peak=round(gb / HBM_PEAK_GBPS, 4))
+        kernels[n] = ent
+    gemm_ms = sum(per_op[n] for n in st.flops)
+    quant_ms = sum(per_op[n] for n in st.bytes)
+    total_flops = sum(st.flops.values())
+    total_bytes = sum(st.bytes.values())
+    value = total_flops / (ms_step * 1e-3) / 1e12
+
+    dom = max(per_op, key=per_op.get)
+    if dom in st.flops:
+        ach = st.flops[dom] / (per_op[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / FP8_PEAK_TFLOPS, 4)}
+    else:
+        ach = st.bytes[dom] / (per_op[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4)}
+    roof["kernel"] = dom
+    roof["traffic"] = None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(d, args.cpu_seconds)
+
+    cfg = {"workload": {
+        "dsv3": "DeepSeek-V3-shaped local expert slice: 32 experts, hidden 7168, intermediate "
+                "2048, 16384 routed token rows (Zipf 1.1 group sizes); FP8 forward + "
+                "weight-gradient + MXFP8 forward",
+        "dense": "Llama3-8B-style FFN GEMM: M=8192, K=4096, N=14336, G=1; FP8 forward",
+        "moe16b": "DeepSeek-MoE-16B-shaped experts: 64 experts, K=2048, N=1408, 49152 routed "
+                  "rows (top-6, Zipf 1.1); FP8 forward",
+        "tiny": "4 experts, K=256, N=512, 1024 token rows; e4m3fnuz forward + weight-gradient",
+    }[args.workload], "M": d["M"], "K": d["K"], "N": d["N"], "experts": d["E"],
+        "fp8_format": "e4m3fn" if d["fmt"] == 1 else "e4m3fnuz"}
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8e4m3fn x fp8e4m3fn -> fp32 acc" if d["fmt"] == 1 else
+                 "fp8e4m3fnuz -> fp32 acc",
+        "data": "synthetic (seeded; device-drawn N(0,1) activations/gradients, N(0,0.02) "
+                "weights; Zipf-routed group offsets)",
+        "config": cfg,
+        "quantize_GBps": round(total_bytes / (quant_ms * 1e-3) / 1e9, 1),
+        "quantize_frac_hbm_peak": round(total_bytes / (quant_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "gemm_TFLOPs": round(total_flops / (gemm_ms * 1e-3) / 1e12, 1),
+        "gemm_frac_mfma_peak": round(total_flops / (gemm_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

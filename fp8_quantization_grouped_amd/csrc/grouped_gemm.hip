@@ -5,55 +5,91 @@
 // to experts; fosswire.org "AMD Primus adds FP8/MXFP8 kernels ...", section "What Primus adds
 // for MoE training on MI355X": FP8 and MXFP8 grouped GEMM for the expert FFNs).
 //
-// Both operands are contraction-contiguous byte matrices ("row" = one output row or column):
+// Both operands are contraction-contiguous byte matrices:
 //   forward, M-grouped:  out[m,n]   = sum_k A[m,k] * B_g[n,k] / (sa[m] * sb[g,n]),  m in group g
 //   wgrad, K-grouped:    out[g,k,n] = sum_{m in g} A[k,m] * B[n,m] / (sa[g,k] * sb[g,n])
 //   MX forward:          out[m,n]   = sum_kb 2^(ea+eb) sum_{k in kb} A[m,k] * B_g[n,k]
 //
-// Kernel: 256 threads (4 waves in 2x2), a 128x128 output tile per block, contraction steps of
-// 128 bytes.  Each step, every lane fetches 4 16-byte chunks of each operand tile into
-// registers (the next step's fetch is in flight while the current step computes), stores them
-// into a double-buffered LDS tile (row r, chunk c at position c ^ (r & 7): the eight 16-byte
-// reads of a fragment load hit distinct banks), and each wave runs 4x4
-// v_mfma_f32_16x16x128_f8f6f4 (OCP e4m3 operands; the block-scaled form for MX) over its 64x64
-// sub-tile.  Operand lane layout of that instruction on gfx950 (established with one-hot
-// inputs): lane l holds row l%16; its bytes 0-15 are K offsets 16*(l/16)+[0,16) and bytes 16-31
-// are K offsets 64+16*(l/16)+[0,16); lane r+16b supplies the E8M0 scale of row r, K block b;
-// result register i of lane l is row 4*(l/16)+i, column l%16.
+// Kernel (one 256-thread block = 4 waves per CU):
+//   * 256x256 output tile, 128-byte contraction steps, each wave owns a 128x128 sub-tile
+//     (64 v_mfma_f32_16x16x128_f8f6f4 per step; 256 fp32 accumulators per lane).
+//   * Operand tiles go HBM/L2 -> LDS directly with buffer_load_dwordx4 ... lds (no staging
+//     registers), double-buffered: the loads of step k+1 are issued right after the barrier of
+//     step k and are waited for only after step k's matrix work, so one barrier per step.
+//     Rows and chunks outside the operand are turned into out-of-range buffer offsets and
+//     read back as zeros.  LDS position of (row r, 16-byte chunk c) is r*128 + 16*(c ^ (r&7)),
+//     so the fragment reads (16 rows x one chunk per instruction group) hit distinct banks.
+//   * The MFMA's A operand is the N-side tile and its B operand the M-side tile, so result
+//     register i of lane l is output row l%16, column 4*(l/16)+i: each lane holds four
+//     consecutive outputs of one row and the epilogue stores them as one 8-byte bf16 quad.
+//   * Tiles are numbered so that each XCD (blocks are dealt round-robin to the 8 XCDs) gets a
+//     contiguous run of tiles: the 32 CUs of an XCD share operand tiles in their L2.
+//   * Operand lane layout of the 16x16x128 f8f6f4 instruction on gfx950 (established with
+//     one-hot inputs): lane l holds row l%16; its bytes 0-15 are K offsets 16*(l/16)+[0,16) and
+//     bytes 16-31 are K offsets 64+16*(l/16)+[0,16); lane r+16b supplies the E8M0 scale of row
+//     r, K block b.
 //
-// e4m3fnuz operands: gfx950's matrix cores read OCP e4m3 only (byte 0x7F, the fnuz 240 code, is
-// NaN there), so fnuz bytes are re-encoded to the e4m3fn byte of the same value while staging
-// into LDS: exponent field - 1 for fnuz exponents >= 2 (exact), and the nearest e4m3fn
-// subnormal (ties to even) for fnuz values below 2^-6, which moves a product by at most 2^-10
+// e4m3fnuz operands: the matrix cores read OCP e4m3 only (byte 0x7F, the fnuz 240 code, is NaN
+// there), so fnuz fragments are re-encoded to the e4m3fn byte of the same value after the LDS
+// read: exponent field - 1 for fnuz exponents >= 2 (exact), and the nearest e4m3fn subnormal
+// (ties to even) for fnuz values below 2^-6, which moves a product by at most 2^-10
 // quantization units.
 //
-// Group scheduling stays on the device (no host read of the offsets): the forward grid has
-// ceil(M/128) + G row-tile slots, each block finds its (group, row tile) with a block-wide scan
-// of per-group tile counts, and surplus slots exit.  Offsets are clamped into [0, M] before use.
+// Weight gradient: a group's token range starts and ends anywhere, so the chunk holding the
+// first (last) token of the group can carry neighbouring groups' bytes; those bytes of the
+// activation operand are zeroed in LDS on the (at most two) edge steps of a tile.
+//
+// Group scheduling stays on the device (no host read of the offsets): the forward grid covers
+// ceil(M/256) + G row-tile slots per column tile, each block finds its (group, row tile) with a
+// block-wide scan of per-group tile counts, and surplus slots exit.  Offsets are clamped into
+// [0, M] before use, so any offsets content keeps every access in range.
 #include "common.hpp"
 
 namespace fp8q {
 
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float v4f_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int GB_M = 128, GB_N = 128, GB_K = 128;
+constexpr int GT = 256;         // output tile edge (rows and columns)
+constexpr int GK = 128;         // contraction bytes per step
+constexpr int STAGE = GT * GK;  // bytes of one operand tile in LDS
+constexpr uint32_t OOB = 0x80000000u;
 constexpr int MODE_FWD = 0, MODE_WGRAD = 1;
 
-// Bytes of `w` at positions base..base+3 kept where lo <= pos < hi.
-__device__ __forceinline__ uint32_t keep_mask4(int lo, int hi, int base) {
-    int a = lo - base, b = hi - base;
-    a = a < 0 ? 0 : (a > 4 ? 4 : a);
-    b = b < 0 ? 0 : (b > 4 ? 4 : b);
-    const uint32_t below_b = b >= 4 ? 0xFFFFFFFFu : ((1u << (8 * b)) - 1u);
-    const uint32_t from_a = a >= 4 ? 0u : (0xFFFFFFFFu << (8 * a));
-    return below_b & from_a;
+// 16-byte slot of chunk c in row r: c ^ (r & 7) ^ ((r >> 3) & 1).  Sixteen consecutive rows
+// at one chunk then land in sixteen distinct 16-byte bank slots (64 x 4-byte banks), and any
+// eight consecutive rows in eight distinct slots (32 banks).
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int lds_off(int r, int ch) { return r * GK + ((ch ^ swz(r)) << 4); }
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t make_rsrc4(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;  // block-uniform: keep the descriptor in SGPRs
+    return i32x4_t{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                   __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)),
+                   __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
 }
-__device__ __forceinline__ void mask_chunk(uint4& v, int lo, int hi) {
-    v.x &= keep_mask4(lo, hi, 0);
-    v.y &= keep_mask4(lo, hi, 4);
-    v.z &= keep_mask4(lo, hi, 8);
-    v.w &= keep_mask4(lo, hi, 12);
+// 16 bytes per lane from a buffer straight into LDS at lds_base + 16*lane (lds_base is
+// wave-uniform).  Written as inline assembly so that the compiler does not order every later
+// LDS read after it: the waits are explicit (s_waitcnt vmcnt before the step's barrier).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)p);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
 }
 
 // e4m3fnuz byte -> e4m3fn byte of the same value (four bytes at a time).
@@ -68,246 +104,415 @@ __device__ __forceinline__ uint32_t fnuz_to_fn4(uint32_t w) {
     const uint32_t small = (half + rnd) | sign;
     return (normal & m8) | (small & ~m8);
 }
-__device__ __forceinline__ void fnuz_to_fn(uint4& v) {
-    v.x = fnuz_to_fn4(v.x);
-    v.y = fnuz_to_fn4(v.y);
-    v.z = fnuz_to_fn4(v.z);
-    v.w = fnuz_to_fn4(v.w);
+
+// Bytes at positions base..base+3 of a chunk kept where lo <= pos < hi.
+__device__ __forceinline__ uint32_t keep_mask4(int lo, int hi, int base) {
+    int a = lo - base, b = hi - base;
+    a = a < 0 ? 0 : (a > 4 ? 4 : a);
+    b = b < 0 ? 0 : (b > 4 ? 4 : b);
+    const uint32_t below_b = b >= 4 ? 0xFFFFFFFFu : ((1u << (8 * b)) - 1u);
+    const uint32_t from_a = a >= 4 ? 0u : (0xFFFFFFFFu << (8 * a));
+    return below_b & from_a;
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
+    a += 0x7FFFu + ((a >> 16) & 1u);
+    b += 0x7FFFu + ((b >> 16) & 1u);
+    return (a >> 16) | (b & 0xFFFF0000u);
 }
 
-__device__ __forceinline__ int lds_off(int r, int ch) { return r * GB_K + ((ch ^ (r & 7)) << 4); }
+__device__ __forceinline__ v8i_t frag(const uint8_t* tile, int r, int kg, bool fnuz) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(tile + lds_off(r, kg));
+    const uint4 hi = *reinterpret_cast<const uint4*>(tile + lds_off(r, 4 + kg));
+    v8i_t f = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    if (fnuz) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) f[i] = (int)fnuz_to_fn4((uint32_t)f[i]);
+    }
+    return f;
+}
 
-template <int FMT, int MODE, bool MX>
-__global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(
-    const uint8_t* __restrict__ a, int64_t lda, const float* __restrict__ a_scales,
-    const uint8_t* __restrict__ a_e8, int64_t ld_sa, const uint8_t* __restrict__ b, int64_t ldb,
-    int64_t bgs, const float* __restrict__ b_scales, const uint8_t* __restrict__ b_e8,
-    int64_t ld_sb, int64_t sbgs, const int32_t* __restrict__ offsets, int G, int64_t M,
-    int64_t N, int64_t K, uint16_t* __restrict__ c, int64_t ldc) {
-    __shared__ __align__(16) uint8_t smem[2][2][GB_M * GB_K];
-    __shared__ int s_scan[256];
-    __shared__ int s_info[2];
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
+struct GemmArgs {
+    const uint8_t* a;
+    int64_t lda;
+    const float* a_scales;
+    const uint8_t* a_e8;
+    int64_t ld_sa;
+    const uint8_t* b;
+    int64_t ldb;
+    int64_t bgs;
+    const float* b_scales;
+    const uint8_t* b_e8;
+    int64_t ld_sb;
+    int64_t sbgs;
+    const int32_t* offsets;
+    int G;
+    int64_t M, N, K;
+    uint16_t* c;
+    int64_t ldc;
+    int nt_n;         // column tiles
+    int nt_k;         // wgrad: row tiles along K
+    bool vec_store;   // 8-byte aligned output quads
+};
 
+constexpr int GMAX = 2048;  // groups whose schedule prefix fits in LDS
+
+// Group g's token rows, clamped into [0, M] so that any offsets content stays in range.
+__device__ __forceinline__ void group_rows(const GemmArgs& p, int g, int64_t& lo, int64_t& hi) {
+    lo = g == 0 ? 0 : (int64_t)p.offsets[g - 1];
+    lo = lo < 0 ? 0 : (lo > p.M ? p.M : lo);
+    hi = p.offsets[g];
+    hi = hi < lo ? lo : (hi > p.M ? p.M : hi);
+}
+
+struct Tile {
     int g;
-    int64_t row_lo, row_hi, kb_lo, kb_hi, kstart;
-    const int64_t n0 = (int64_t)blockIdx.y * GB_N;
-    if (MODE == MODE_FWD) {
-        const int slot = blockIdx.x;
-        if (t == 0) s_info[0] = -1;
-        int base = 0;
-        for (int g0 = 0; g0 < G; g0 += 256) {
-            const int gg = g0 + t;
-            int cnt = 0;
-            if (gg < G) {
-                int64_t lo = gg == 0 ? 0 : (int64_t)offsets[gg - 1];
-                lo = lo < 0 ? 0 : (lo > M ? M : lo);
-                int64_t hi = offsets[gg];
-                hi = hi < lo ? lo : (hi > M ? M : hi);
-                cnt = (int)((hi - lo + GB_M - 1) / GB_M);
+    int64_t row_lo, row_hi, n0, kb_lo, kb_hi, kstart, nk, a_rows, b_rows;
+};
+
+// One block per CU runs a contiguous range of the tile sequence (persistent schedule).
+// Forward: tile t = (row-tile slot, column tile) with the column tile fastest, every tile the
+// same work; weight gradient: tiles ordered by group, each weighted by its contraction steps
+// plus one for its epilogue, so the ranges split the real work evenly whatever the group
+// sizes.  Ranges of one XCD are adjacent (blocks are dealt to XCDs round-robin), so concurrent
+// tiles share operand tiles in that XCD's L2.  The first contraction step of a block's next
+// tile is fetched while the current tile finishes.
+template <int FMT, int MODE, bool MX>
+__global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
+    __shared__ __align__(16) uint8_t smem[2][2][STAGE];
+    __shared__ __align__(16) uint32_t sscale[2][2][GT];  // MX: 4 E8M0 bytes per row and step
+    __shared__ long long s_pref[GMAX + 1];                 // per-group prefix of tiles / work
+    __shared__ long long s_part[256];
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    constexpr bool FNUZ = FMT == FP8Q_E4M3FNUZ;
+    const int64_t tiles_per_group = (int64_t)p.nt_k * p.nt_n;
+
+    // --- schedule prefix: forward = row-tile slots per group; wgrad = work units per group
+    if (t == 0) s_pref[0] = 0;
+    long long base = 0;
+    for (int g0 = 0; g0 < p.G; g0 += 256) {
+        const int gg = g0 + t;
+        long long cnt = 0;
+        if (gg < p.G) {
+            int64_t lo, hi;
+            group_rows(p, gg, lo, hi);
+            if (MODE == MODE_FWD) {
+                cnt = (hi - lo + GT - 1) / GT;
+            } else {
+                const int64_t ks = lo & ~(int64_t)15;
+                const int64_t nk = hi > ks ? (hi - ks + GK - 1) / GK : 0;
+                cnt = tiles_per_group * (nk + 1);
             }
-            __syncthreads();
-            s_scan[t] = cnt;
-            __syncthreads();
-            for (int off = 1; off < 256; off <<= 1) {
-                const int add = t >= off ? s_scan[t - off] : 0;
-                __syncthreads();
-                s_scan[t] += add;
-                __syncthreads();
-            }
-            const int incl = s_scan[t];
-            if (cnt > 0 && slot >= base + incl - cnt && slot < base + incl) {
-                s_info[0] = gg;
-                s_info[1] = slot - (base + incl - cnt);
-            }
-            base += s_scan[255];
         }
         __syncthreads();
-        g = s_info[0];
-        if (g < 0) return;  // surplus slot (block-uniform)
-        int64_t glo = g == 0 ? 0 : (int64_t)offsets[g - 1];
-        glo = glo < 0 ? 0 : (glo > M ? M : glo);
-        int64_t ghi = offsets[g];
-        ghi = ghi < glo ? glo : (ghi > M ? M : ghi);
-        row_lo = glo + (int64_t)s_info[1] * GB_M;
-        row_hi = row_lo + GB_M < ghi ? row_lo + GB_M : ghi;
-        kb_lo = 0;
-        kb_hi = K;
-        kstart = 0;
-    } else {
-        g = blockIdx.z;
-        row_lo = (int64_t)blockIdx.x * GB_M;
-        row_hi = row_lo + GB_M < K ? row_lo + GB_M : K;
-        int64_t glo = g == 0 ? 0 : (int64_t)offsets[g - 1];
-        glo = glo < 0 ? 0 : (glo > M ? M : glo);
-        int64_t ghi = offsets[g];
-        ghi = ghi < glo ? glo : (ghi > M ? M : ghi);
-        kb_lo = glo;
-        kb_hi = ghi;
-        kstart = glo & ~(int64_t)15;
-    }
-    const int64_t nk = kb_hi > kstart ? (kb_hi - kstart + GB_K - 1) / GB_K : 0;
-    const uint8_t* bbase = MODE == MODE_FWD ? b + (int64_t)g * bgs : b;
-
-    v4f_t acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-    uint4 ra[4], rb[4];
-    int sa_cur[4], sb_cur[4], sa_nxt[4], sb_nxt[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) sa_cur[i] = sb_cur[i] = sa_nxt[i] = sb_nxt[i] = 127;
-
-    auto gload = [&](int64_t kpos) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int id = t + 256 * i, r = id >> 3, ch = id & 7;
-            const int64_t p = kpos + 16 * ch;
-            const bool kin = p < kb_hi && p + 16 > kb_lo;
-            const bool edge = p < kb_lo || p + 16 > kb_hi;
-            const int64_t ar = row_lo + r;
-            uint4 va = make_uint4(0, 0, 0, 0);
-            if (kin && ar < row_hi) {
-                va = *reinterpret_cast<const uint4*>(a + ar * lda + p);
-                if (edge) mask_chunk(va, (int)(kb_lo - p), (int)(kb_hi - p));
-                if (FMT == FP8Q_E4M3FNUZ) fnuz_to_fn(va);
-            }
-            ra[i] = va;
-            const int64_t bn = n0 + r;
-            uint4 vb = make_uint4(0, 0, 0, 0);
-            if (kin && bn < N) {
-                vb = *reinterpret_cast<const uint4*>(bbase + bn * ldb + p);
-                if (edge) mask_chunk(vb, (int)(kb_lo - p), (int)(kb_hi - p));
-                if (FMT == FP8Q_E4M3FNUZ) fnuz_to_fn(vb);
-            }
-            rb[i] = vb;
-        }
-        if (MX) {
-            const int64_t kb = kpos / 32 + (lane >> 4);
-            const bool kbin = kpos + 32 * (lane >> 4) < K;
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int64_t ar = row_lo + wm * 64 + i * 16 + (lane & 15);
-                sa_nxt[i] = (kbin && ar < row_hi) ? (int)a_e8[ar * ld_sa + kb] : 127;
-                const int64_t bn = n0 + wn * 64 + i * 16 + (lane & 15);
-                sb_nxt[i] = (kbin && bn < N) ? (int)b_e8[(int64_t)g * sbgs + bn * ld_sb + kb] : 127;
-            }
-        }
-    };
-    auto sstore = [&](int stage) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int id = t + 256 * i, r = id >> 3, ch = id & 7;
-            *reinterpret_cast<uint4*>(&smem[stage][0][lds_off(r, ch)]) = ra[i];
-            *reinterpret_cast<uint4*>(&smem[stage][1][lds_off(r, ch)]) = rb[i];
-        }
-    };
-
-    if (nk > 0) {
-        gload(kstart);
-        sstore(0);
-    }
-    for (int64_t kk = 0; kk < nk; kk++) {
-        const int cur = (int)(kk & 1);
-        if (MX) {
-#pragma unroll
-            for (int i = 0; i < 4; i++) { sa_cur[i] = sa_nxt[i]; sb_cur[i] = sb_nxt[i]; }
-        }
-        if (kk + 1 < nk) gload(kstart + (kk + 1) * GB_K);
+        s_part[t] = cnt;
         __syncthreads();
-        const uint8_t* As = smem[cur][0];
-        const uint8_t* Bs = smem[cur][1];
-        const int kg = lane >> 4;
-        v8i_t af[4], bfr[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int ra_ = wm * 64 + i * 16 + (lane & 15);
-            const uint4 lo = *reinterpret_cast<const uint4*>(&As[lds_off(ra_, kg)]);
-            const uint4 hi = *reinterpret_cast<const uint4*>(&As[lds_off(ra_, 4 + kg)]);
-            af[i] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                          (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            const int rb_ = wn * 64 + i * 16 + (lane & 15);
-            const uint4 blo = *reinterpret_cast<const uint4*>(&Bs[lds_off(rb_, kg)]);
-            const uint4 bhi = *reinterpret_cast<const uint4*>(&Bs[lds_off(rb_, 4 + kg)]);
-            bfr[i] = v8i_t{(int)blo.x, (int)blo.y, (int)blo.z, (int)blo.w,
-                           (int)bhi.x, (int)bhi.y, (int)bhi.z, (int)bhi.w};
+        for (int off = 1; off < 256; off <<= 1) {
+            const long long add = t >= off ? s_part[t - off] : 0;
+            __syncthreads();
+            s_part[t] += add;
+            __syncthreads();
         }
+        if (gg < p.G) s_pref[gg + 1] = base + s_part[t];
+        base += s_part[255];
+    }
+    __syncthreads();
+    const long long total = MODE == MODE_FWD ? s_pref[p.G] * p.nt_n : s_pref[p.G];
+    const int nb = gridDim.x;
+    const int r = (nb % 8 == 0) ? (int)(blockIdx.x % 8) * (nb / 8) + (int)(blockIdx.x / 8)
+                                : (int)blockIdx.x;
+    const long long w_lo = total * r / nb, w_hi = total * (r + 1) / nb;
+
+    // --- tile iteration state
+    // forward: tile index; wgrad: (group, local tile) with start work s_pref[g] + local*unit
+    long long ti = w_lo;
+    int wg = 0;
+    long long wl = 0;
+    if (MODE == MODE_WGRAD) {
+        int lo = 0, hi = p.G - 1;  // last group whose work starts at or before w_lo
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_pref[mid] <= w_lo) lo = mid; else hi = mid - 1;
+        }
+        wg = lo;
+        int64_t glo, ghi;
+        group_rows(p, wg, glo, ghi);
+        const int64_t ks = glo & ~(int64_t)15;
+        const long long unit = (ghi > ks ? (ghi - ks + GK - 1) / GK : 0) + 1;
+        wl = (w_lo - s_pref[wg] + unit - 1) / unit;
+    }
+    // Returns false when the block's range is exhausted.
+    auto next_tile = [&](Tile& T) -> bool {
+        if (MODE == MODE_FWD) {
+            if (ti >= w_hi) return false;
+            const long long slot = ti / p.nt_n;
+            T.n0 = (ti % p.nt_n) * GT;
+            int lo = 0, hi = p.G - 1;  // last group whose slots start at or before slot
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_pref[mid] <= slot) lo = mid; else hi = mid - 1;
+            }
+            T.g = lo;
+            int64_t glo, ghi;
+            group_rows(p, T.g, glo, ghi);
+            T.row_lo = glo + (slot - s_pref[T.g]) * GT;
+            T.row_hi = T.row_lo + GT < ghi ? T.row_lo + GT : ghi;
+            T.kb_lo = 0;
+            T.kb_hi = p.K;
+            T.kstart = 0;
+            T.a_rows = p.M - T.row_lo < GT ? p.M - T.row_lo : GT;
+            ti++;
+        } else {
+            while (wg < p.G && wl >= tiles_per_group) { wg++; wl = 0; }
+            if (wg >= p.G) return false;
+            int64_t glo, ghi;
+            group_rows(p, wg, glo, ghi);
+            const int64_t ks = glo & ~(int64_t)15;
+            const long long unit = (ghi > ks ? (ghi - ks + GK - 1) / GK : 0) + 1;
+            if (s_pref[wg] + wl * unit >= w_hi) return false;
+            T.g = wg;
+            T.row_lo = (wl / p.nt_n) * GT;
+            T.n0 = (wl % p.nt_n) * GT;
+            T.row_hi = T.row_lo + GT < p.K ? T.row_lo + GT : p.K;
+            T.kb_lo = glo;
+            T.kb_hi = ghi;
+            T.kstart = ks;
+            T.a_rows = T.row_hi - T.row_lo;
+            wl++;
+        }
+        T.nk = T.kb_hi > T.kstart ? (T.kb_hi - T.kstart + GK - 1) / GK : 0;
+        T.b_rows = p.N - T.n0 < GT ? p.N - T.n0 : GT;
+        return true;
+    };
+
+    uint32_t sa_pack = 0, sb_pack = 0;
+    // Step starting at kpos of tile T into LDS stage `stage`: this lane's chunk of each of the
+    // 8 load instructions goes to LDS slot (wave*8+i)*64 + lane.
+    auto issue = [&](const Tile& T, int64_t kpos, int stage) {
+        // Buffer resources rebased at the tile's first rows (offsets stay 32-bit).  Forward
+        // rows of A past row_hi belong to other groups: they are read (finite data) but their
+        // outputs are never stored; only rows past the operand's end are out of range.
+        const i32x4_t ra = make_rsrc4(p.a + T.row_lo * p.lda, (uint32_t)(T.a_rows * p.lda));
+        const i32x4_t rb = make_rsrc4(
+            p.b + (MODE == MODE_FWD ? (int64_t)T.g * p.bgs : 0) + T.n0 * p.ldb,
+            (uint32_t)(T.b_rows * p.ldb));
+        uint8_t* As = smem[stage][0];
+        uint8_t* Bs = smem[stage][1];
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+        for (int i = 0; i < 8; i++) {
+            const int row = (wave * 8 + i) * 8 + (lane >> 3);
+            const int ch = (lane & 7) ^ swz(row);
+            const int64_t pk = kpos + 16 * ch;
+            const bool kin = pk < T.kb_hi && pk + 16 > T.kb_lo;
+            const uint32_t aoff = (kin && row < T.a_rows) ? (uint32_t)(row * p.lda + pk) : OOB;
+            const uint32_t boff = (kin && row < T.b_rows) ? (uint32_t)(row * p.ldb + pk) : OOB;
+            dma16(ra, aoff, lds_addr(As + (wave * 8 + i) * 1024));
+            dma16(rb, boff, lds_addr(Bs + (wave * 8 + i) * 1024));
+        }
+        if (MX) {
+            // rows t of both tiles: the 4 E8M0 bytes of this 128-byte step, packed into one
+            // dword per row (blocks past K get 127 = 2^0: their data bytes are zero)
+            const __amdgpu_buffer_rsrc_t rsa =
+                make_rsrc(p.a_e8 + T.row_lo * p.ld_sa, (uint32_t)(T.a_rows * p.ld_sa));
+            const __amdgpu_buffer_rsrc_t rsb =
+                make_rsrc(p.b_e8 + (int64_t)T.g * p.sbgs + T.n0 * p.ld_sb,
+                          (uint32_t)(T.b_rows * p.ld_sb));
+            const int64_t kb0 = kpos / 32;
+            sa_pack = sb_pack = 0;
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-                if (MX)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        af[i], bfr[j], acc[i][j], 0, 0, 0, sa_cur[i], 0, sb_cur[j]);
-                else
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        af[i], bfr[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+                const bool ok = kpos + 32 * j < p.K;
+                const uint32_t oa = (ok && t < T.a_rows) ? (uint32_t)(t * p.ld_sa + kb0 + j) : OOB;
+                const uint32_t ob = (ok && t < T.b_rows) ? (uint32_t)(t * p.ld_sb + kb0 + j) : OOB;
+                const uint32_t ea =
+                    ok ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rsa, oa, 0, 0) : 127u;
+                const uint32_t eb =
+                    ok ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rsb, ob, 0, 0) : 127u;
+                sa_pack |= ea << (8 * j);
+                sb_pack |= eb << (8 * j);
             }
-        if (kk + 1 < nk) sstore(cur ^ 1);
-    }
+        }
+    };
+    // MX scales are staged in registers and written to LDS after the step's matrix work.
+    auto commit_scales = [&](int stage) {
+        if (MX) {
+            sscale[stage][0][t] = sa_pack;
+            sscale[stage][1][t] = sb_pack;
+        }
+    };
 
-    // Epilogue: dequantize (multiply by the reciprocal scales) and round to bf16.
-    float csc[4];
-    int64_t gn[4];
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        gn[j] = n0 + wn * 64 + j * 16 + (lane & 15);
-        csc[j] = 1.0f;
-        if (!MX && gn[j] < N) csc[j] = 1.0f / b_scales[(int64_t)g * N + gn[j]];
+    Tile cur, nxt;
+    bool have = next_tile(cur);
+    int stage0 = 0;  // LDS stage holding the current tile's first step
+    if (have && cur.nk > 0) {
+        issue(cur, cur.kstart, 0);
+        commit_scales(0);
     }
+    const int kg = lane >> 4, lr = lane & 15, lq = lane >> 4;
+    while (have) {
+        v4f_t acc[8][8];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+        for (int i = 0; i < 8; i++)
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const int64_t gm = row_lo + wm * 64 + i * 16 + 4 * (lane >> 4) + e;
-            if (gm >= row_hi) continue;
-            float rsc = 1.0f;
+            for (int j = 0; j < 8; j++) acc[i][j] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+        bool have_next = false, next_issued = false;
+
+        for (int64_t kk = 0; kk < cur.nk; kk++) {
+            const int cur_st = (stage0 + (int)(kk & 1)) & 1;
+            const int64_t kpos = cur.kstart + kk * GK;
+            wait_vm0();  // this wave's loads of step kk have landed
+            if (MODE == MODE_WGRAD && (kpos < cur.kb_lo || kpos + GK > cur.kb_hi)) {
+                // zero the activation bytes of neighbouring groups in the straddling chunks
+                __syncthreads();
+                const int lo = (int)(cur.kb_lo - kpos), hi = (int)(cur.kb_hi - kpos);
+#pragma unroll
+                for (int ch = 0; ch < 8; ch++) {
+                    const int b0 = 16 * ch;
+                    if ((lo > b0 && lo < b0 + 16) || (hi > b0 && hi < b0 + 16)) {
+                        uint4* q = reinterpret_cast<uint4*>(&smem[cur_st][0][lds_off(t, ch)]);
+                        uint4 w = *q;
+                        w.x &= keep_mask4(lo, hi, b0);
+                        w.y &= keep_mask4(lo, hi, b0 + 4);
+                        w.z &= keep_mask4(lo, hi, b0 + 8);
+                        w.w &= keep_mask4(lo, hi, b0 + 12);
+                        *q = w;
+                    }
+                }
+            }
+            __syncthreads();
+            if (kk + 1 < cur.nk) {
+                issue(cur, kpos + GK, cur_st ^ 1);
+            } else {
+                have_next = next_tile(nxt);
+                if (have_next && nxt.nk > 0) {
+                    issue(nxt, nxt.kstart, cur_st ^ 1);
+                    next_issued = true;
+                }
+            }
+
+            const uint8_t* As = smem[cur_st][0];
+            const uint8_t* Bs = smem[cur_st][1];
+            const bool kb_in = kpos + 32 * kg < cur.kb_hi;  // MX: this lane's K block exists
+            v8i_t bf[8];
+            int sb_[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const int rn = wn * 128 + j * 16 + lr;
+                bf[j] = frag(Bs, rn, kg, FNUZ);
+                if (MX) sb_[j] = kb_in ? (int)((sscale[cur_st][1][rn] >> (8 * kg)) & 0xFFu) : 127;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int rm = wm * 128 + i * 16 + lr;
+                const v8i_t af = frag(As, rm, kg, FNUZ);
+                int sa_ = 0;
+                if (MX) sa_ = kb_in ? (int)((sscale[cur_st][0][rm] >> (8 * kg)) & 0xFFu) : 127;
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    if (MX)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            bf[j], af, acc[i][j], 0, 0, 0, sb_[j], 0, sa_);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            bf[j], af, acc[i][j], 0, 0, 0, 0, 0, 0);
+                }
+            }
+            if (kk + 1 < cur.nk || next_issued) commit_scales(cur_st ^ 1);
+        }
+        if (cur.nk == 0) {
+            // nothing was computed; start the next tile's first step in the free stage
+            have_next = next_tile(nxt);
+            if (have_next && nxt.nk > 0) {
+                issue(nxt, nxt.kstart, stage0);
+                commit_scales(stage0);
+            }
+        }
+
+        // Epilogue: lane holds rows row_lo + wm*128 + 16i + lane%16, columns
+        // n0 + wn*128 + 16j + 4*(lane/16) + 0..3.  Dequantize and store 4 bf16 at once.
+        float4 cs[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int64_t n = cur.n0 + wn * 128 + j * 16 + 4 * lq;
+            float s4[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                s4[e] = (!MX && n + e < p.N) ? 1.0f / p.b_scales[(int64_t)cur.g * p.N + n + e] : 1.0f;
+            cs[j] = make_float4(s4[0], s4[1], s4[2], s4[3]);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int64_t m = cur.row_lo + wm * 128 + i * 16 + lr;
+            if (m >= cur.row_hi) continue;
+            float rs = 1.0f;
             uint16_t* crow;
             if (MODE == MODE_FWD) {
-                if (!MX) rsc = 1.0f / a_scales[gm];
-                crow = c + gm * ldc;
+                if (!MX) rs = 1.0f / p.a_scales[m];
+                crow = p.c + m * p.ldc;
             } else {
-                rsc = 1.0f / a_scales[(int64_t)g * K + gm];
-                crow = c + ((int64_t)g * K + gm) * ldc;
+                rs = 1.0f / p.a_scales[(int64_t)cur.g * p.K + m];
+                crow = p.c + ((int64_t)cur.g * p.K + m) * p.ldc;
             }
 #pragma unroll
-            for (int j = 0; j < 4; j++)
-                if (gn[j] < N) crow[gn[j]] = f32_to_bf16_rne(acc[i][j][e] * rsc * csc[j]);
+            for (int j = 0; j < 8; j++) {
+                const int64_t n = cur.n0 + wn * 128 + j * 16 + 4 * lq;
+                const float y0 = acc[i][j][0] * rs * cs[j].x, y1 = acc[i][j][1] * rs * cs[j].y;
+                const float y2 = acc[i][j][2] * rs * cs[j].z, y3 = acc[i][j][3] * rs * cs[j].w;
+                const uint32_t w0 = pack_bf16x2(y0, y1), w1 = pack_bf16x2(y2, y3);
+                if (p.vec_store && n + 3 < p.N) {
+                    *reinterpret_cast<uint2*>(crow + n) = make_uint2(w0, w1);
+                } else {
+                    if (n < p.N) crow[n] = (uint16_t)w0;
+                    if (n + 1 < p.N) crow[n + 1] = (uint16_t)(w0 >> 16);
+                    if (n + 2 < p.N) crow[n + 2] = (uint16_t)w1;
+                    if (n + 3 < p.N) crow[n + 3] = (uint16_t)(w1 >> 16);
+                }
+            }
         }
+        stage0 = (stage0 + (int)(cur.nk & 1)) & 1;
+        have = have_next;
+        cur = nxt;
     }
 }
 
-template <int FMT, int MODE, bool MX>
-static fp8q_status_t launch_gemm(const uint8_t* a, int64_t lda, const float* sa,
-                                 const uint8_t* a_e8, int64_t ld_sa, const uint8_t* b,
-                                 int64_t ldb, int64_t bgs, const float* sb, const uint8_t* b_e8,
-                                 int64_t ld_sb, int64_t sbgs, const int32_t* offsets, int G,
-                                 int64_t M, int64_t N, int64_t K, uint16_t* c, int64_t ldc,
-                                 hipStream_t stream) {
-    dim3 grid;
-    if (MODE == MODE_FWD) {
-        const int64_t slots = (M + GB_M - 1) / GB_M + G;
-        const int64_t nt = (N + GB_N - 1) / GB_N;
-        if (slots > 0x7FFFFFFFLL || nt > 65535) return FP8Q_ERR_UNSUPPORTED;
-        grid = dim3((unsigned)slots, (unsigned)nt, 1);
-    } else {
-        const int64_t kt = (K + GB_M - 1) / GB_M;
-        const int64_t nt = (N + GB_N - 1) / GB_N;
-        if (kt > 0x7FFFFFFFLL || nt > 65535 || G > 65535) return FP8Q_ERR_UNSUPPORTED;
-        grid = dim3((unsigned)kt, (unsigned)nt, (unsigned)G);
+static int num_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cached[dev] = n;
     }
-    grouped_gemm_kernel<FMT, MODE, MX><<<grid, dim3(256), 0, stream>>>(
-        a, lda, sa, a_e8, ld_sa, b, ldb, bgs, sb, b_e8, ld_sb, sbgs, offsets, G, M, N, K, c, ldc);
+    return cached[dev];
+}
+
+template <int FMT, int MODE, bool MX>
+static fp8q_status_t launch_gemm(GemmArgs p, hipStream_t stream) {
+    p.nt_n = (int)((p.N + GT - 1) / GT);
+    p.nt_k = MODE == MODE_FWD ? 1 : (int)((p.K + GT - 1) / GT);
+    if (p.G > GMAX) return FP8Q_ERR_UNSUPPORTED;
+    // Upper bound of tiles (forward: each group may add one partial row tile).
+    const int64_t tiles = MODE == MODE_FWD ? ((p.M + GT - 1) / GT + p.G) * p.nt_n
+                                           : (int64_t)p.G * p.nt_k * p.nt_n;
+    int64_t grid = num_cus();
+    if (tiles < grid) grid = tiles;
+    if (grid < 1) grid = 1;
+    p.vec_store = (p.ldc % 4 == 0) && fp8q_aligned(p.c, 8);
+    gemm256_kernel<FMT, MODE, MX><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p);
     FP8Q_CHECK_LAUNCH();
     return FP8Q_OK;
+}
+
+// 32-bit buffer offsets: a 256-row tile of either operand must span less than 2^31 bytes.
+static inline bool offsets_fit(int64_t lda, int64_t ldb) {
+    return (int64_t)GT * lda < 0x7FFFFFFFLL && (int64_t)GT * ldb < 0x7FFFFFFFLL;
 }
 
 }  // namespace fp8q
@@ -321,36 +526,29 @@ extern "C" fp8q_status_t fp8_grouped_gemm(fp8q_gemm_mode_t mode, fp8q_format_t f
     using namespace fp8q;
     if (!fp8q_fmt_ok(fmt) || groups < 1 || M < 0 || N < 0 || K < 0 || ldc < N || !offsets)
         return FP8Q_ERR_INVALID_ARG;
+    GemmArgs p{};
+    p.a = a; p.lda = lda; p.a_scales = a_scales; p.b = b; p.ldb = ldb; p.bgs = b_group_stride;
+    p.b_scales = b_scales; p.offsets = offsets; p.G = groups; p.M = M; p.N = N; p.K = K;
+    p.c = c; p.ldc = ldc;
     if (mode == FP8Q_GEMM_FWD_MGROUPED) {
         if (lda < K || ldb < K || b_group_stride < 0) return FP8Q_ERR_INVALID_ARG;
         if (M == 0 || N == 0) return FP8Q_OK;
         if (!a || !b || !a_scales || !b_scales || !c) return FP8Q_ERR_INVALID_ARG;
         if (K % 16 || lda % 16 || ldb % 16 || b_group_stride % 16 || !fp8q_aligned(a, 16) ||
-            !fp8q_aligned(b, 16))
+            !fp8q_aligned(b, 16) || !offsets_fit(lda, ldb))
             return FP8Q_ERR_UNSUPPORTED;
-        if (fmt == FP8Q_E4M3FN)
-            return launch_gemm<FP8Q_E4M3FN, MODE_FWD, false>(a, lda, a_scales, nullptr, 0, b, ldb,
-                                                           b_group_stride, b_scales, nullptr, 0,
-                                                           0, offsets, groups, M, N, K, c, ldc,
-                                                           stream);
-        return launch_gemm<FP8Q_E4M3FNUZ, MODE_FWD, false>(a, lda, a_scales, nullptr, 0, b, ldb,
-                                                         b_group_stride, b_scales, nullptr, 0, 0,
-                                                         offsets, groups, M, N, K, c, ldc, stream);
+        if (fmt == FP8Q_E4M3FN) return launch_gemm<FP8Q_E4M3FN, MODE_FWD, false>(p, stream);
+        return launch_gemm<FP8Q_E4M3FNUZ, MODE_FWD, false>(p, stream);
     }
     if (mode == FP8Q_GEMM_WGRAD_KGROUPED) {
         if (lda < M || ldb < M || b_group_stride != 0) return FP8Q_ERR_INVALID_ARG;
         if (K == 0 || N == 0) return FP8Q_OK;
         if (!a_scales || !b_scales || !c || (M > 0 && (!a || !b))) return FP8Q_ERR_INVALID_ARG;
-        if (lda % 16 || ldb % 16 || !fp8q_aligned(a, 16) || !fp8q_aligned(b, 16))
+        if (lda % 16 || ldb % 16 || !fp8q_aligned(a, 16) || !fp8q_aligned(b, 16) ||
+            !offsets_fit(lda, ldb))
             return FP8Q_ERR_UNSUPPORTED;
-        if (fmt == FP8Q_E4M3FN)
-            return launch_gemm<FP8Q_E4M3FN, MODE_WGRAD, false>(a, lda, a_scales, nullptr, 0, b,
-                                                             ldb, 0, b_scales, nullptr, 0, 0,
-                                                             offsets, groups, M, N, K, c, ldc,
-                                                             stream);
-        return launch_gemm<FP8Q_E4M3FNUZ, MODE_WGRAD, false>(a, lda, a_scales, nullptr, 0, b, ldb,
-                                                           0, b_scales, nullptr, 0, 0, offsets,
-                                                           groups, M, N, K, c, ldc, stream);
+        if (fmt == FP8Q_E4M3FN) return launch_gemm<FP8Q_E4M3FN, MODE_WGRAD, false>(p, stream);
+        return launch_gemm<FP8Q_E4M3FNUZ, MODE_WGRAD, false>(p, stream);
     }
     return FP8Q_ERR_INVALID_ARG;
 }
@@ -370,10 +568,11 @@ extern "C" fp8q_status_t fp8_mx_grouped_gemm(const uint8_t* a, int64_t lda, cons
     if (M == 0 || N == 0) return FP8Q_OK;
     if (!a || !b || !a_e8m0 || !b_e8m0 || !c) return FP8Q_ERR_INVALID_ARG;
     if (lda % 16 || ldb % 16 || b_group_stride % 16 || !fp8q_aligned(a, 16) ||
-        !fp8q_aligned(b, 16))
+        !fp8q_aligned(b, 16) || !offsets_fit(lda, ldb) || !offsets_fit(ld_sa, ld_sb))
         return FP8Q_ERR_UNSUPPORTED;
-    return launch_gemm<FP8Q_E4M3FN, MODE_FWD, true>(a, lda, nullptr, a_e8m0, ld_sa, b, ldb,
-                                                   b_group_stride, nullptr, b_e8m0, ld_sb,
-                                                   sb_group_stride, offsets, groups, M, N, K, c,
-                                                   ldc, stream);
+    GemmArgs p{};
+    p.a = a; p.lda = lda; p.a_e8 = a_e8m0; p.ld_sa = ld_sa; p.b = b; p.ldb = ldb;
+    p.bgs = b_group_stride; p.b_e8 = b_e8m0; p.ld_sb = ld_sb; p.sbgs = sb_group_stride;
+    p.offsets = offsets; p.G = groups; p.M = M; p.N = N; p.K = K; p.c = c; p.ldc = ldc;
+    return launch_gemm<FP8Q_E4M3FN, MODE_FWD, true>(p, stream);
 }
