@@ -62,6 +62,15 @@ constexpr int MODE_FWD = 0, MODE_WGRAD = 1;
 // eight consecutive rows in eight distinct slots (32 banks).
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int lds_off(int r, int ch) { return r * GK + ((ch ^ swz(r)) << 4); }
+// N-side tile: its fragments take rows 32j' + 8q + 4h + e (q = lane%16 / 4, e = lane%4) so that
+// each lane's results are 8 consecutive output columns; slot c ^ (2*((r>>3)&3) + ((r>>1)&1))
+// puts those 16 rows in 16 distinct 16-byte bank slots.
+__device__ __forceinline__ int swzB(int r) { return (((r >> 3) & 3) << 1) | ((r >> 1) & 1); }
+__device__ __forceinline__ int lds_offB(int r, int ch) { return r * GK + ((ch ^ swzB(r)) << 4); }
+// Row of the N-side tile that feeds MFMA row lr of column block j (see swzB).
+__device__ __forceinline__ int brow(int j, int lr) {
+    return 32 * (j >> 1) + 8 * (lr >> 2) + 4 * (j & 1) + (lr & 3);
+}
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4_t make_rsrc4(const void* base, uint32_t bytes) {
@@ -82,6 +91,12 @@ __device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t voff, uint32_t lds_
                  : "memory", "m0");
 }
 #pragma clang diagnostic pop
+__device__ __forceinline__ void dma4(i32x4_t rsrc, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)p);
@@ -122,9 +137,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (a >> 16) | (b & 0xFFFF0000u);
 }
 
+template <bool NSIDE>
 __device__ __forceinline__ v8i_t frag(const uint8_t* tile, int r, int kg, bool fnuz) {
-    const uint4 lo = *reinterpret_cast<const uint4*>(tile + lds_off(r, kg));
-    const uint4 hi = *reinterpret_cast<const uint4*>(tile + lds_off(r, 4 + kg));
+    const uint4 lo = *reinterpret_cast<const uint4*>(tile + (NSIDE ? lds_offB(r, kg) : lds_off(r, kg)));
+    const uint4 hi =
+        *reinterpret_cast<const uint4*>(tile + (NSIDE ? lds_offB(r, 4 + kg) : lds_off(r, 4 + kg)));
     v8i_t f = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     if (fnuz) {
@@ -154,7 +171,7 @@ struct GemmArgs {
     int64_t ldc;
     int nt_n;         // column tiles
     int nt_k;         // wgrad: row tiles along K
-    bool vec_store;   // 8-byte aligned output quads
+    bool vec_store;   // 16-byte aligned output octets
 };
 
 constexpr int GMAX = 2048;  // groups whose schedule prefix fits in LDS
@@ -167,9 +184,9 @@ __device__ __forceinline__ void group_rows(const GemmArgs& p, int g, int64_t& lo
     hi = hi < lo ? lo : (hi > p.M ? p.M : hi);
 }
 
-struct Tile {
-    int g;
-    int64_t row_lo, row_hi, n0, kb_lo, kb_hi, kstart, nk, a_rows, b_rows;
+struct Tile {  // all extents < 2^31 (checked on the host)
+    int g, par;  // group; parity of the tile in the block's sequence (scale buffer)
+    int row_lo, row_hi, n0, kb_lo, kb_hi, kstart, nk, a_rows, b_rows;
 };
 
 // One block per CU runs a contiguous range of the tile sequence (persistent schedule).
@@ -182,7 +199,9 @@ struct Tile {
 template <int FMT, int MODE, bool MX>
 __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
     __shared__ __align__(16) uint8_t smem[2][2][STAGE];
-    __shared__ __align__(16) uint32_t sscale[2][2][GT];  // MX: 4 E8M0 bytes per row and step
+    // MX: 4 E8M0 bytes per row and step (by stage); otherwise the fp32 dequant scales of the
+    // tile's rows [0] and columns [1] (by tile parity)
+    __shared__ __align__(16) uint32_t sscale[2][2][GT];
     __shared__ long long s_pref[GMAX + 1];                 // per-group prefix of tiles / work
     __shared__ long long s_part[256];
     const int t = threadIdx.x, lane = t & 63;
@@ -222,35 +241,41 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
     }
     __syncthreads();
     const long long total = MODE == MODE_FWD ? s_pref[p.G] * p.nt_n : s_pref[p.G];
+    // The work is split evenly over the XCDs (blocks are dealt to the 8 XCDs round-robin);
+    // inside an XCD's contiguous range the tiles are dealt round-robin to its blocks, so the
+    // tiles running at the same moment are neighbours and share operand tiles in that L2.
     const int nb = gridDim.x;
-    const int r = (nb % 8 == 0) ? (int)(blockIdx.x % 8) * (nb / 8) + (int)(blockIdx.x / 8)
-                                : (int)blockIdx.x;
-    const long long w_lo = total * r / nb, w_hi = total * (r + 1) / nb;
-
-    // --- tile iteration state
-    // forward: tile index; wgrad: (group, local tile) with start work s_pref[g] + local*unit
-    long long ti = w_lo;
-    int wg = 0;
-    long long wl = 0;
-    if (MODE == MODE_WGRAD) {
-        int lo = 0, hi = p.G - 1;  // last group whose work starts at or before w_lo
+    const int nx = nb % 8 == 0 ? 8 : 1;
+    const int xcd = nx == 8 ? (int)(blockIdx.x % 8) : 0;
+    const int lb = nx == 8 ? (int)(blockIdx.x / 8) : (int)blockIdx.x;
+    const int bpx = nb / nx;  // blocks per XCD
+    const long long w_lo = total * xcd / nx, w_hi = total * (xcd + 1) / nx;
+    // First tile whose work starts at or after w, as a global tile index (wgrad: tiles are
+    // numbered group by group, tiles_per_group each).
+    auto first_tile_at = [&](long long w) -> long long {
+        if (MODE == MODE_FWD) return w;
+        if (w >= total) return (long long)p.G * tiles_per_group;
+        int lo = 0, hi = p.G - 1;  // last group whose work starts at or before w
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (s_pref[mid] <= w_lo) lo = mid; else hi = mid - 1;
+            if (s_pref[mid] <= w) lo = mid; else hi = mid - 1;
         }
-        wg = lo;
         int64_t glo, ghi;
-        group_rows(p, wg, glo, ghi);
+        group_rows(p, lo, glo, ghi);
         const int64_t ks = glo & ~(int64_t)15;
         const long long unit = (ghi > ks ? (ghi - ks + GK - 1) / GK : 0) + 1;
-        wl = (w_lo - s_pref[wg] + unit - 1) / unit;
-    }
-    // Returns false when the block's range is exhausted.
+        const long long l = (w - s_pref[lo] + unit - 1) / unit;
+        return (long long)lo * tiles_per_group + l;  // may equal the next group's first tile
+    };
+    const long long t_end = first_tile_at(w_hi);
+    const long long first_ti = first_tile_at(w_lo) + lb;
+    long long ti = first_ti;
+    // Returns false when the block's share is exhausted.
     auto next_tile = [&](Tile& T) -> bool {
+        if (ti >= t_end) return false;
         if (MODE == MODE_FWD) {
-            if (ti >= w_hi) return false;
             const long long slot = ti / p.nt_n;
-            T.n0 = (ti % p.nt_n) * GT;
+            T.n0 = (int)(ti % p.nt_n) * GT;
             int lo = 0, hi = p.G - 1;  // last group whose slots start at or before slot
             while (lo < hi) {
                 const int mid = (lo + hi + 1) >> 1;
@@ -259,69 +284,78 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
             T.g = lo;
             int64_t glo, ghi;
             group_rows(p, T.g, glo, ghi);
-            T.row_lo = glo + (slot - s_pref[T.g]) * GT;
-            T.row_hi = T.row_lo + GT < ghi ? T.row_lo + GT : ghi;
+            T.row_lo = (int)(glo + (slot - s_pref[T.g]) * GT);
+            T.row_hi = T.row_lo + GT < ghi ? T.row_lo + GT : (int)ghi;
             T.kb_lo = 0;
-            T.kb_hi = p.K;
+            T.kb_hi = (int)p.K;
             T.kstart = 0;
-            T.a_rows = p.M - T.row_lo < GT ? p.M - T.row_lo : GT;
-            ti++;
+            T.a_rows = p.M - T.row_lo < GT ? (int)(p.M - T.row_lo) : GT;
         } else {
-            while (wg < p.G && wl >= tiles_per_group) { wg++; wl = 0; }
-            if (wg >= p.G) return false;
+            T.g = (int)(ti / tiles_per_group);
+            const long long l = ti % tiles_per_group;
             int64_t glo, ghi;
-            group_rows(p, wg, glo, ghi);
-            const int64_t ks = glo & ~(int64_t)15;
-            const long long unit = (ghi > ks ? (ghi - ks + GK - 1) / GK : 0) + 1;
-            if (s_pref[wg] + wl * unit >= w_hi) return false;
-            T.g = wg;
-            T.row_lo = (wl / p.nt_n) * GT;
-            T.n0 = (wl % p.nt_n) * GT;
-            T.row_hi = T.row_lo + GT < p.K ? T.row_lo + GT : p.K;
-            T.kb_lo = glo;
-            T.kb_hi = ghi;
-            T.kstart = ks;
+            group_rows(p, T.g, glo, ghi);
+            T.row_lo = (int)(l / p.nt_n) * GT;
+            T.n0 = (int)(l % p.nt_n) * GT;
+            T.row_hi = T.row_lo + GT < p.K ? T.row_lo + GT : (int)p.K;
+            T.kb_lo = (int)glo;
+            T.kb_hi = (int)ghi;
+            T.kstart = (int)(glo & ~(int64_t)15);
             T.a_rows = T.row_hi - T.row_lo;
-            wl++;
         }
+        T.par = (int)(((ti - first_ti) / bpx) & 1);
+        ti += bpx;
         T.nk = T.kb_hi > T.kstart ? (T.kb_hi - T.kstart + GK - 1) / GK : 0;
-        T.b_rows = p.N - T.n0 < GT ? p.N - T.n0 : GT;
+        T.b_rows = p.N - T.n0 < GT ? (int)(p.N - T.n0) : GT;
         return true;
     };
 
     uint32_t sa_pack = 0, sb_pack = 0;
     // Step starting at kpos of tile T into LDS stage `stage`: this lane's chunk of each of the
     // 8 load instructions goes to LDS slot (wave*8+i)*64 + lane.
-    auto issue = [&](const Tile& T, int64_t kpos, int stage) {
+    auto issue = [&](const Tile& T, int kpos, int stage) {
         // Buffer resources rebased at the tile's first rows (offsets stay 32-bit).  Forward
         // rows of A past row_hi belong to other groups: they are read (finite data) but their
         // outputs are never stored; only rows past the operand's end are out of range.
-        const i32x4_t ra = make_rsrc4(p.a + T.row_lo * p.lda, (uint32_t)(T.a_rows * p.lda));
+        const i32x4_t ra =
+            make_rsrc4(p.a + (int64_t)T.row_lo * p.lda, (uint32_t)(T.a_rows * p.lda));
         const i32x4_t rb = make_rsrc4(
-            p.b + (MODE == MODE_FWD ? (int64_t)T.g * p.bgs : 0) + T.n0 * p.ldb,
+            p.b + (MODE == MODE_FWD ? (int64_t)T.g * p.bgs : 0) + (int64_t)T.n0 * p.ldb,
             (uint32_t)(T.b_rows * p.ldb));
         uint8_t* As = smem[stage][0];
         uint8_t* Bs = smem[stage][1];
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             const int row = (wave * 8 + i) * 8 + (lane >> 3);
-            const int ch = (lane & 7) ^ swz(row);
-            const int64_t pk = kpos + 16 * ch;
-            const bool kin = pk < T.kb_hi && pk + 16 > T.kb_lo;
-            const uint32_t aoff = (kin && row < T.a_rows) ? (uint32_t)(row * p.lda + pk) : OOB;
-            const uint32_t boff = (kin && row < T.b_rows) ? (uint32_t)(row * p.ldb + pk) : OOB;
+            const int cha = (lane & 7) ^ swz(row), chb = (lane & 7) ^ swzB(row);
+            const int pa = kpos + 16 * cha, pb = kpos + 16 * chb;
+            const bool ka = pa < T.kb_hi && pa + 16 > T.kb_lo;
+            const bool kb = pb < T.kb_hi && pb + 16 > T.kb_lo;
+            const uint32_t aoff =
+                (ka && row < T.a_rows) ? (uint32_t)row * (uint32_t)p.lda + (uint32_t)pa : OOB;
+            const uint32_t boff =
+                (kb && row < T.b_rows) ? (uint32_t)row * (uint32_t)p.ldb + (uint32_t)pb : OOB;
             dma16(ra, aoff, lds_addr(As + (wave * 8 + i) * 1024));
             dma16(rb, boff, lds_addr(Bs + (wave * 8 + i) * 1024));
+        }
+        if (!MX && kpos == T.kstart) {
+            // the tile's dequant scales (row t of each side) ride along with its first step
+            const int64_t sm0 = MODE == MODE_FWD ? (int64_t)T.row_lo : (int64_t)T.g * p.K + T.row_lo;
+            const i32x4_t rsm = make_rsrc4(p.a_scales + sm0, (uint32_t)(T.row_hi - T.row_lo) * 4u);
+            const i32x4_t rsn = make_rsrc4(p.b_scales + (int64_t)T.g * p.N + T.n0,
+                                           (uint32_t)T.b_rows * 4u);
+            dma4(rsm, (uint32_t)t * 4u, lds_addr(&sscale[T.par][0][wave * 64]));
+            dma4(rsn, (uint32_t)t * 4u, lds_addr(&sscale[T.par][1][wave * 64]));
         }
         if (MX) {
             // rows t of both tiles: the 4 E8M0 bytes of this 128-byte step, packed into one
             // dword per row (blocks past K get 127 = 2^0: their data bytes are zero)
             const __amdgpu_buffer_rsrc_t rsa =
-                make_rsrc(p.a_e8 + T.row_lo * p.ld_sa, (uint32_t)(T.a_rows * p.ld_sa));
+                make_rsrc(p.a_e8 + (int64_t)T.row_lo * p.ld_sa, (uint32_t)(T.a_rows * p.ld_sa));
             const __amdgpu_buffer_rsrc_t rsb =
-                make_rsrc(p.b_e8 + (int64_t)T.g * p.sbgs + T.n0 * p.ld_sb,
+                make_rsrc(p.b_e8 + (int64_t)T.g * p.sbgs + (int64_t)T.n0 * p.ld_sb,
                           (uint32_t)(T.b_rows * p.ld_sb));
-            const int64_t kb0 = kpos / 32;
+            const int kb0 = kpos / 32;
             sa_pack = sb_pack = 0;
 #pragma unroll
             for (int j = 0; j < 4; j++) {
@@ -361,14 +395,14 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
             for (int j = 0; j < 8; j++) acc[i][j] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
         bool have_next = false, next_issued = false;
 
-        for (int64_t kk = 0; kk < cur.nk; kk++) {
-            const int cur_st = (stage0 + (int)(kk & 1)) & 1;
-            const int64_t kpos = cur.kstart + kk * GK;
+        for (int kk = 0; kk < cur.nk; kk++) {
+            const int cur_st = (stage0 + (kk & 1)) & 1;
+            const int kpos = cur.kstart + kk * GK;
             wait_vm0();  // this wave's loads of step kk have landed
             if (MODE == MODE_WGRAD && (kpos < cur.kb_lo || kpos + GK > cur.kb_hi)) {
                 // zero the activation bytes of neighbouring groups in the straddling chunks
                 __syncthreads();
-                const int lo = (int)(cur.kb_lo - kpos), hi = (int)(cur.kb_hi - kpos);
+                const int lo = cur.kb_lo - kpos, hi = cur.kb_hi - kpos;
 #pragma unroll
                 for (int ch = 0; ch < 8; ch++) {
                     const int b0 = 16 * ch;
@@ -401,14 +435,14 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
             int sb_[8];
 #pragma unroll
             for (int j = 0; j < 8; j++) {
-                const int rn = wn * 128 + j * 16 + lr;
-                bf[j] = frag(Bs, rn, kg, FNUZ);
+                const int rn = wn * 128 + brow(j, lr);
+                bf[j] = frag<true>(Bs, rn, kg, FNUZ);
                 if (MX) sb_[j] = kb_in ? (int)((sscale[cur_st][1][rn] >> (8 * kg)) & 0xFFu) : 127;
             }
 #pragma unroll
             for (int i = 0; i < 8; i++) {
                 const int rm = wm * 128 + i * 16 + lr;
-                const v8i_t af = frag(As, rm, kg, FNUZ);
+                const v8i_t af = frag<false>(As, rm, kg, FNUZ);
                 int sa_ = 0;
                 if (MX) sa_ = kb_in ? (int)((sscale[cur_st][0][rm] >> (8 * kg)) & 0xFFu) : 127;
 #pragma unroll
@@ -424,7 +458,10 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
             if (kk + 1 < cur.nk || next_issued) commit_scales(cur_st ^ 1);
         }
         if (cur.nk == 0) {
-            // nothing was computed; start the next tile's first step in the free stage
+            // nothing was computed; start the next tile's first step in the free stage once
+            // every wave is past the previous tile's epilogue (it read the scale buffer the
+            // next tile's scales go to)
+            __syncthreads();
             have_next = next_tile(nxt);
             if (have_next && nxt.nk > 0) {
                 issue(nxt, nxt.kstart, stage0);
@@ -432,48 +469,46 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
             }
         }
 
-        // Epilogue: lane holds rows row_lo + wm*128 + 16i + lane%16, columns
-        // n0 + wn*128 + 16j + 4*(lane/16) + 0..3.  Dequantize and store 4 bf16 at once.
-        float4 cs[8];
+        // Epilogue: lane holds rows row_lo + wm*128 + 16i + lane%16 and, per column-block pair
+        // j', the 8 consecutive columns n0 + wn*128 + 32j' + 8*(lane/16) + 0..7 (blocks 2j' and
+        // 2j'+1 give 4 each).  Dequantize with the reciprocal scales and store 8 bf16 at once.
+        const float* s_rows = reinterpret_cast<const float*>(sscale[cur.par][0]);
+        const float* s_cols = reinterpret_cast<const float*>(sscale[cur.par][1]);
+        const bool scaled = !MX && cur.nk > 0;  // an empty contraction stores zeros
+        float rs[8];
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const int64_t n = cur.n0 + wn * 128 + j * 16 + 4 * lq;
-            float s4[4];
+        for (int i = 0; i < 8; i++)
+            rs[i] = scaled ? __builtin_amdgcn_rcpf(s_rows[wm * 128 + i * 16 + lr]) : 1.0f;
 #pragma unroll
-            for (int e = 0; e < 4; e++)
-                s4[e] = (!MX && n + e < p.N) ? 1.0f / p.b_scales[(int64_t)cur.g * p.N + n + e] : 1.0f;
-            cs[j] = make_float4(s4[0], s4[1], s4[2], s4[3]);
-        }
+        for (int jp = 0; jp < 4; jp++) {
+            const int n = cur.n0 + wn * 128 + 32 * jp + 8 * lq;
+            float cs[8];
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const int64_t m = cur.row_lo + wm * 128 + i * 16 + lr;
-            if (m >= cur.row_hi) continue;
-            float rs = 1.0f;
-            uint16_t* crow;
-            if (MODE == MODE_FWD) {
-                if (!MX) rs = 1.0f / p.a_scales[m];
-                crow = p.c + m * p.ldc;
-            } else {
-                rs = 1.0f / p.a_scales[(int64_t)cur.g * p.K + m];
-                crow = p.c + ((int64_t)cur.g * p.K + m) * p.ldc;
-            }
+            for (int e = 0; e < 8; e++)
+                cs[e] = scaled ? __builtin_amdgcn_rcpf(s_cols[wn * 128 + 32 * jp + 8 * lq + e]) : 1.0f;
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const int64_t n = cur.n0 + wn * 128 + j * 16 + 4 * lq;
-                const float y0 = acc[i][j][0] * rs * cs[j].x, y1 = acc[i][j][1] * rs * cs[j].y;
-                const float y2 = acc[i][j][2] * rs * cs[j].z, y3 = acc[i][j][3] * rs * cs[j].w;
-                const uint32_t w0 = pack_bf16x2(y0, y1), w1 = pack_bf16x2(y2, y3);
-                if (p.vec_store && n + 3 < p.N) {
-                    *reinterpret_cast<uint2*>(crow + n) = make_uint2(w0, w1);
+            for (int i = 0; i < 8; i++) {
+                const int m = cur.row_lo + wm * 128 + i * 16 + lr;
+                if (m >= cur.row_hi) continue;
+                uint16_t* crow =
+                    p.c + (MODE == MODE_FWD ? (int64_t)m : (int64_t)cur.g * p.K + m) * p.ldc;
+                const v4f_t a0 = acc[i][2 * jp], a1 = acc[i][2 * jp + 1];
+                const float r_ = rs[i];
+                const uint32_t w0 = pack_bf16x2(a0[0] * r_ * cs[0], a0[1] * r_ * cs[1]);
+                const uint32_t w1 = pack_bf16x2(a0[2] * r_ * cs[2], a0[3] * r_ * cs[3]);
+                const uint32_t w2 = pack_bf16x2(a1[0] * r_ * cs[4], a1[1] * r_ * cs[5]);
+                const uint32_t w3 = pack_bf16x2(a1[2] * r_ * cs[6], a1[3] * r_ * cs[7]);
+                if (p.vec_store && n + 7 < p.N) {
+                    *reinterpret_cast<uint4*>(crow + n) = make_uint4(w0, w1, w2, w3);
                 } else {
-                    if (n < p.N) crow[n] = (uint16_t)w0;
-                    if (n + 1 < p.N) crow[n + 1] = (uint16_t)(w0 >> 16);
-                    if (n + 2 < p.N) crow[n + 2] = (uint16_t)w1;
-                    if (n + 3 < p.N) crow[n + 3] = (uint16_t)(w1 >> 16);
+                    const uint32_t w[4] = {w0, w1, w2, w3};
+#pragma unroll
+                    for (int e = 0; e < 8; e++)
+                        if (n + e < p.N) crow[n + e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
                 }
             }
         }
-        stage0 = (stage0 + (int)(cur.nk & 1)) & 1;
+        stage0 = (stage0 + (cur.nk & 1)) & 1;
         have = have_next;
         cur = nxt;
     }
@@ -497,14 +532,15 @@ template <int FMT, int MODE, bool MX>
 static fp8q_status_t launch_gemm(GemmArgs p, hipStream_t stream) {
     p.nt_n = (int)((p.N + GT - 1) / GT);
     p.nt_k = MODE == MODE_FWD ? 1 : (int)((p.K + GT - 1) / GT);
-    if (p.G > GMAX) return FP8Q_ERR_UNSUPPORTED;
+    if (p.G > GMAX || p.M > 0x7FFFFFFFLL || p.N > 0x7FFFFFFFLL || p.K > 0x7FFFFFFFLL)
+        return FP8Q_ERR_UNSUPPORTED;
     // Upper bound of tiles (forward: each group may add one partial row tile).
     const int64_t tiles = MODE == MODE_FWD ? ((p.M + GT - 1) / GT + p.G) * p.nt_n
                                            : (int64_t)p.G * p.nt_k * p.nt_n;
     int64_t grid = num_cus();
     if (tiles < grid) grid = tiles;
     if (grid < 1) grid = 1;
-    p.vec_store = (p.ldc % 4 == 0) && fp8q_aligned(p.c, 8);
+    p.vec_store = (p.ldc % 8 == 0) && fp8q_aligned(p.c, 16);
     gemm256_kernel<FMT, MODE, MX><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p);
     FP8Q_CHECK_LAUNCH();
     return FP8Q_OK;
