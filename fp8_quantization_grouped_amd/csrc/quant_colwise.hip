@@ -11,17 +11,22 @@
 //
 // gfx950 design.  A column's absmax needs every row of its group before any element can be
 // cast, and a group can span thousands of rows, so the work is two passes over 256x64 tiles:
-//   1. colwise_amax_kernel: each block loads a 256-row x 64-column tile (8 rows x 8 columns per
-//      lane, 16-byte loads, 128 contiguous bytes per row), reduces each group segment of the
-//      tile to 64 column maxima (packed 16-bit max on bf16 magnitude bits, lane shuffles, then
-//      LDS across the 4 waves) and publishes them with relaxed device-scope atomicMax on the
-//      bf16 magnitude bits (exact: for finite values their integer order is the value order).
-//   2. colwise_cast_kernel: reloads the tile, turns the finished maxima into scales (per group
-//      in LDS), scales/clamps/converts along rows so each lane holds 8 consecutive output
-//      bytes of each of its 8 columns, transposes through LDS and writes 16-byte chunks of
-//      the column-major output (16 lanes cover one column's 256 contiguous bytes).
-// The block whose tile contains a group's first row writes that group's scales; the last row
-// tile also writes groups that start at the end (trailing empty groups).
+//   1. colwise_amax_kernel: each block walks 4 consecutive 256-row x 64-column tiles (8 rows x
+//      8 columns per lane, 16-byte loads, 128 contiguous bytes per row, the next tile's loads
+//      in flight while the current one is reduced), keeps per-lane column maxima of the group
+//      it is in (packed 16-bit max on bf16 magnitude bits), and when the group changes reduces
+//      them to 64 column maxima (lane shuffles, then LDS across the 4 waves) and publishes them
+//      with relaxed device-scope atomicMax on the bf16 magnitude bits (exact: for finite values
+//      their integer order is the value order).
+//   2. colwise_cast_kernel: walks the same tiles, turns the finished maxima into scales (per
+//      group in LDS, reused while the groups do not change), scales/clamps/converts along rows
+//      so each lane holds 8 consecutive output bytes of each of its 8 columns, transposes
+//      through LDS and writes 16-byte chunks of the column-major output (16 lanes cover one
+//      column's 256 contiguous bytes).
+// The group offsets are staged in LDS once per block, so finding a row's group is a short
+// search in LDS instead of a chain of dependent global loads.  The block whose tile contains
+// a group's first row writes that group's scales; the last row tile also writes groups that
+// start at the end (trailing empty groups).
 #include "common.hpp"
 
 namespace fp8q {
@@ -30,6 +35,53 @@ constexpr int CW_TR = 256;              // tile rows
 constexpr int CW_TC = 64;               // tile columns
 constexpr int CW_STR = CW_TR + 16;      // LDS bytes per transposed column (16-byte aligned)
 constexpr int CW_GB = 8;                // groups per scale batch in LDS
+constexpr int CW_TPB = 4;               // row tiles per block
+constexpr int CW_GLDS = 2048;           // groups whose offsets are staged in LDS
+
+// Group offsets as the kernels read them: from an LDS copy staged once per block (LDS, the
+// usual case: G <= CW_GLDS) or straight from global memory.  The two are separate template
+// instances and the LDS copy is a file-scope __shared__ array referenced by name, so every
+// access compiles to a DS or a global instruction.  Never a generic (flat) pointer that may
+// point into LDS: a flat access is routed by the aperture of its base address register, and
+// the compiler folds "base - 4" + "offset:4" forms (for o[g-1] / o[g] pairs) whose base lies
+// just below the LDS aperture when g == 0.
+__shared__ int cw_s_off[CW_GLDS];
+
+template <bool LDS>
+struct Offs {
+    const int32_t* __restrict__ g;
+    int G;
+    __device__ __forceinline__ int64_t end(int i) const {
+        return LDS ? (int64_t)cw_s_off[i] : (int64_t)g[i];
+    }
+    __device__ __forceinline__ int64_t start(int i) const { return i == 0 ? 0 : end(i - 1); }
+    // first g with end(g) > r, clamped to [0, G-1] (any offsets content stays in range)
+    __device__ __forceinline__ int group_of(int64_t r) const {
+        int lo = 0, hi = G - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (end(mid) > r) hi = mid; else lo = mid + 1;
+        }
+        return lo;
+    }
+    // first group whose start row is >= r (G if none)
+    __device__ __forceinline__ int first_starting_at(int64_t r) const {
+        int lo = 0, hi = G;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (start(mid) >= r) hi = mid; else lo = mid + 1;
+        }
+        return lo;
+    }
+};
+template <bool LDS>
+__device__ __forceinline__ Offs<LDS> stage_offsets(const int32_t* __restrict__ offsets, int G) {
+    if (LDS) {
+        for (int i = threadIdx.x; i < G; i += 256) cw_s_off[i] = offsets[i];
+        __syncthreads();
+    }
+    return Offs<LDS>{offsets, G};
+}
 
 // The lane's 8x8 block: rows r0 + 8*qd + i (i < 8), columns c0 + 8*o .. +7, as bf16 bits
 // packed two per dword (column 2d in the low half of dword d).  Out-of-range elements are 0.
@@ -59,42 +111,25 @@ __global__ void cw_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
         p[i] = 0u;
 }
 
-template <bool VEC>
+template <bool VEC, bool LDS>
 __global__ __launch_bounds__(256) void colwise_amax_kernel(const uint16_t* __restrict__ x,
                                                            int64_t R, int64_t C, int64_t ld_x,
                                                            const int32_t* __restrict__ offsets,
                                                            int G, uint32_t* __restrict__ amax) {
     const int t = threadIdx.x, o = t & 7, qd = t >> 3, lane = t & 63, wave = t >> 6;
-    const int64_t r0 = (int64_t)blockIdx.x * CW_TR, c0 = (int64_t)blockIdx.y * CW_TC;
-    uint4 v[8];
-    cw_load<VEC>(x, R, C, ld_x, r0, c0, o, qd, v);
-    const int64_t r_end = r0 + CW_TR < R ? r0 + CW_TR : R;
-    const int g_first = group_of_row(offsets, G, r0);
-    const int g_last = group_of_row(offsets, G, r_end - 1);
+    const int64_t rb = (int64_t)blockIdx.x * CW_TR * CW_TPB, c0 = (int64_t)blockIdx.y * CW_TC;
     __shared__ uint32_t red[4][8][4];
-    for (int g = g_first; g <= g_last; g++) {
-        int64_t gs = group_start(offsets, g);
-        int64_t ge = g == G - 1 ? r_end : (int64_t)offsets[g];
-        gs = gs > r0 ? gs : r0;
-        ge = ge < r_end ? ge : r_end;
-        if (gs >= ge) continue;  // block-uniform
-        uint32_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
+    const Offs<LDS> off = stage_offsets<LDS>(offsets, G);
+    // running per-lane maxima of group cur_g (block-uniform), published when the group ends
+    int cur_g = -1;
+    uint32_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
+    auto flush = [&]() {
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const int64_t r = r0 + 8 * qd + i;
-            if (r >= gs && r < ge) {
-                m0 = pk_max_u16(m0, mag2(v[i].x));
-                m1 = pk_max_u16(m1, mag2(v[i].y));
-                m2 = pk_max_u16(m2, mag2(v[i].z));
-                m3 = pk_max_u16(m3, mag2(v[i].w));
-            }
-        }
-#pragma unroll
-        for (int off = 8; off < 64; off <<= 1) {
-            m0 = pk_max_u16(m0, (uint32_t)__shfl_xor((int)m0, off, 64));
-            m1 = pk_max_u16(m1, (uint32_t)__shfl_xor((int)m1, off, 64));
-            m2 = pk_max_u16(m2, (uint32_t)__shfl_xor((int)m2, off, 64));
-            m3 = pk_max_u16(m3, (uint32_t)__shfl_xor((int)m3, off, 64));
+        for (int sh = 8; sh < 64; sh <<= 1) {
+            m0 = pk_max_u16(m0, (uint32_t)__shfl_xor((int)m0, sh, 64));
+            m1 = pk_max_u16(m1, (uint32_t)__shfl_xor((int)m1, sh, 64));
+            m2 = pk_max_u16(m2, (uint32_t)__shfl_xor((int)m2, sh, 64));
+            m3 = pk_max_u16(m3, (uint32_t)__shfl_xor((int)m3, sh, 64));
         }
         if (lane < 8) {
             red[wave][lane][0] = m0;
@@ -105,127 +140,165 @@ __global__ __launch_bounds__(256) void colwise_amax_kernel(const uint16_t* __res
         __syncthreads();
         if (t < 32) {
             const int oo = t >> 2, d = t & 3;
-            uint32_t mm = pk_max_u16(pk_max_u16(red[0][oo][d], red[1][oo][d]),
-                                     pk_max_u16(red[2][oo][d], red[3][oo][d]));
+            const uint32_t mm = pk_max_u16(pk_max_u16(red[0][oo][d], red[1][oo][d]),
+                                           pk_max_u16(red[2][oo][d], red[3][oo][d]));
             const int64_t c = c0 + 8 * oo + 2 * d;
-            uint32_t lo = mm & 0xFFFFu, hi = mm >> 16;
-            uint32_t* dst = amax + (int64_t)g * C + c;
+            const uint32_t lo = mm & 0xFFFFu, hi = mm >> 16;
+            uint32_t* dst = amax + (int64_t)cur_g * C + c;
             if (lo && c < C) __hip_atomic_fetch_max(dst, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (hi && c + 1 < C) __hip_atomic_fetch_max(dst + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
+        m0 = m1 = m2 = m3 = 0;
+    };
+    uint4 v[8], vn[8];
+    cw_load<VEC>(x, R, C, ld_x, rb, c0, o, qd, v);
+    for (int k = 0; k < CW_TPB; k++) {
+        const int64_t r0 = rb + (int64_t)k * CW_TR;
+        if (r0 >= R) break;  // block-uniform
+        if (k + 1 < CW_TPB) cw_load<VEC>(x, R, C, ld_x, r0 + CW_TR, c0, o, qd, vn);
+        const int64_t r_end = r0 + CW_TR < R ? r0 + CW_TR : R;
+        const int g_first = off.group_of(r0);
+        const int g_last = off.group_of(r_end - 1);
+        for (int g = g_first; g <= g_last; g++) {
+            int64_t gs = off.start(g);
+            int64_t ge = g == G - 1 ? r_end : off.end(g);
+            gs = gs > r0 ? gs : r0;
+            ge = ge < r_end ? ge : r_end;
+            if (gs >= ge) continue;  // block-uniform
+            if (g != cur_g) {
+                if (cur_g >= 0) flush();
+                cur_g = g;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int64_t r = r0 + 8 * qd + i;
+                if (r >= gs && r < ge) {
+                    m0 = pk_max_u16(m0, mag2(v[i].x));
+                    m1 = pk_max_u16(m1, mag2(v[i].y));
+                    m2 = pk_max_u16(m2, mag2(v[i].z));
+                    m3 = pk_max_u16(m3, mag2(v[i].w));
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; i++) v[i] = vn[i];
     }
+    if (cur_g >= 0) flush();
 }
 
-// First group whose start row is >= r (G if none); starts are taken as stored.
-__device__ __forceinline__ int first_group_starting_at(const int32_t* __restrict__ offsets, int G,
-                                                       int64_t r) {
-    int lo = 0, hi = G;
-    while (lo < hi) {
-        int mid = (lo + hi) >> 1;
-        if (group_start(offsets, mid) >= r) hi = mid; else lo = mid + 1;
-    }
-    return lo;
-}
-
-template <int FMT, bool VEC, bool VEC_OUT>
+template <int FMT, bool VEC, bool VEC_OUT, bool LDS>
 __global__ __launch_bounds__(256) void colwise_cast_kernel(
     const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ld_x,
     const int32_t* __restrict__ offsets, int G, const uint32_t* __restrict__ amax,
     uint8_t* __restrict__ qt, int64_t ld_qt, float* __restrict__ scales) {
     const int t = threadIdx.x, o = t & 7, qd = t >> 3;
-    const int64_t r0 = (int64_t)blockIdx.x * CW_TR, c0 = (int64_t)blockIdx.y * CW_TC;
+    const int64_t rb = (int64_t)blockIdx.x * CW_TR * CW_TPB, c0 = (int64_t)blockIdx.y * CW_TC;
     __shared__ __align__(16) float sc[CW_GB][CW_TC];
     __shared__ __align__(16) uint8_t tile[CW_TC * CW_STR];
+    const Offs<LDS> off = stage_offsets<LDS>(offsets, G);
 
-    // Scales of the groups this tile owns (first row inside the tile; the last tile also owns
-    // groups starting at or after its end, i.e. trailing empty groups).
+    // Scales of the groups this block owns (first row inside one of its tiles; the block with
+    // the last tile also owns groups starting at or after the end, i.e. trailing empty groups).
     {
-        const bool last_tile = r0 + CW_TR >= R;
-        int g = first_group_starting_at(offsets, G, r0);
-        for (; g < G; g++) {
-            if (!last_tile && group_start(offsets, g) >= r0 + CW_TR) break;
+        const int64_t r_stop = rb + (int64_t)CW_TR * CW_TPB;
+        const bool last_block = r_stop >= R;
+        for (int g = off.first_starting_at(rb); g < G; g++) {
+            if (!last_block && off.start(g) >= r_stop) break;
             if (t < CW_TC && c0 + t < C) {
                 const int64_t idx = (int64_t)g * C + c0 + t;
                 scales[idx] = scale_from_amax<FMT>(__uint_as_float(amax[idx] << 16));
             }
         }
     }
-    if (r0 >= R) return;  // only the R == 0 launch has such a block (block-uniform)
+    if (rb >= R) return;  // only the R == 0 launch has such a block (block-uniform)
 
-    uint4 v[8];
-    cw_load<VEC>(x, R, C, ld_x, r0, c0, o, qd, v);
-    const int64_t r_end = r0 + CW_TR < R ? r0 + CW_TR : R;
-    const int g_first = group_of_row(offsets, G, r0);
-    const int g_last = group_of_row(offsets, G, r_end - 1);
-    // group of each of the lane's rows (-1 past the end)
-    int gid[8];
-    {
-        int g = group_of_row(offsets, G, r0 + 8 * qd);
+    int sc_lo = -1, sc_hi = -2;  // groups held in sc (block-uniform)
+    uint4 v[8], vn[8];
+    cw_load<VEC>(x, R, C, ld_x, rb, c0, o, qd, v);
+    for (int k = 0; k < CW_TPB; k++) {
+        const int64_t r0 = rb + (int64_t)k * CW_TR;
+        if (r0 >= R) break;  // block-uniform
+        if (k + 1 < CW_TPB) cw_load<VEC>(x, R, C, ld_x, r0 + CW_TR, c0, o, qd, vn);
+        const int64_t r_end = r0 + CW_TR < R ? r0 + CW_TR : R;
+        const int g_first = off.group_of(r0);
+        const int g_last = off.group_of(r_end - 1);
+        // group of each of the lane's rows (-1 past the end)
+        int gid[8];
+        {
+            int g = off.group_of(r0 + 8 * qd);
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const int64_t r = r0 + 8 * qd + i;
-            while (g < G - 1 && (int64_t)offsets[g] <= r) g++;
-            gid[i] = r < r_end ? g : -1;
+            for (int i = 0; i < 8; i++) {
+                const int64_t r = r0 + 8 * qd + i;
+                while (g < G - 1 && off.end(g) <= r) g++;
+                gid[i] = r < r_end ? g : -1;
+            }
         }
-    }
-    float y[8][8];
+        float y[8][8];
 #pragma unroll
-    for (int i = 0; i < 8; i++)
+        for (int i = 0; i < 8; i++)
 #pragma unroll
-        for (int j = 0; j < 8; j++) y[i][j] = 0.0f;
-
-    for (int gb = g_first; gb <= g_last; gb += CW_GB) {
-        __syncthreads();  // previous batch finished reading sc
-        for (int idx = t; idx < CW_GB * CW_TC; idx += 256) {
-            const int k = idx / CW_TC, cc = idx % CW_TC;
-            const int g = gb + k;
-            float s = 0.0f;
-            if (g <= g_last && c0 + cc < C)
-                s = scale_from_amax<FMT>(__uint_as_float(amax[(int64_t)g * C + c0 + cc] << 16)) *
-                    Fmt<FMT>::mult;
-            sc[k][cc] = s;
+            for (int j = 0; j < 8; j++) y[i][j] = 0.0f;
+        for (int gb = g_first; gb <= g_last; gb += CW_GB) {
+            const int gb_hi = gb + CW_GB - 1 < g_last ? gb + CW_GB - 1 : g_last;
+            if (!(gb >= sc_lo && gb_hi <= sc_hi)) {
+                __syncthreads();  // previous users of sc are done
+                for (int idx = t; idx < CW_GB * CW_TC; idx += 256) {
+                    const int kk = idx / CW_TC, cc = idx % CW_TC;
+                    const int g = gb + kk;
+                    float s = 0.0f;
+                    if (g < G && c0 + cc < C)
+                        s = scale_from_amax<FMT>(__uint_as_float(amax[(int64_t)g * C + c0 + cc] << 16)) *
+                            Fmt<FMT>::mult;
+                    sc[kk][cc] = s;
+                }
+                __syncthreads();
+                sc_lo = gb;
+                sc_hi = gb + CW_GB - 1;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int kk = gid[i] - sc_lo;
+                if (gid[i] >= gb && gid[i] <= gb_hi) {
+                    const float4 sa = *reinterpret_cast<const float4*>(&sc[kk][8 * o]);
+                    const float4 sb = *reinterpret_cast<const float4*>(&sc[kk][8 * o + 4]);
+                    y[i][0] = bf16_lo(v[i].x) * sa.x;
+                    y[i][1] = bf16_hi(v[i].x) * sa.y;
+                    y[i][2] = bf16_lo(v[i].y) * sa.z;
+                    y[i][3] = bf16_hi(v[i].y) * sa.w;
+                    y[i][4] = bf16_lo(v[i].z) * sb.x;
+                    y[i][5] = bf16_hi(v[i].z) * sb.y;
+                    y[i][6] = bf16_lo(v[i].w) * sb.z;
+                    y[i][7] = bf16_hi(v[i].w) * sb.w;
+                }
+            }
+        }
+        __syncthreads();  // previous tile's transposed bytes have been stored
+        // Encode along rows: column j of the lane gets the bytes of rows 8*qd .. 8*qd+7.
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const uint32_t w0 = enc4<FMT>(y[0][j], y[1][j], y[2][j], y[3][j]);
+            const uint32_t w1 = enc4<FMT>(y[4][j], y[5][j], y[6][j], y[7][j]);
+            *reinterpret_cast<uint2*>(&tile[(8 * o + j) * CW_STR + 8 * qd]) = make_uint2(w0, w1);
         }
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const int k = gid[i] - gb;
-            if (k >= 0 && k < CW_GB) {
-                const float4 sa = *reinterpret_cast<const float4*>(&sc[k][8 * o]);
-                const float4 sb = *reinterpret_cast<const float4*>(&sc[k][8 * o + 4]);
-                y[i][0] = bf16_lo(v[i].x) * sa.x;
-                y[i][1] = bf16_hi(v[i].x) * sa.y;
-                y[i][2] = bf16_lo(v[i].y) * sa.z;
-                y[i][3] = bf16_hi(v[i].y) * sa.w;
-                y[i][4] = bf16_lo(v[i].z) * sb.x;
-                y[i][5] = bf16_hi(v[i].z) * sb.y;
-                y[i][6] = bf16_lo(v[i].w) * sb.z;
-                y[i][7] = bf16_hi(v[i].w) * sb.w;
+        for (int kq = 0; kq < 4; kq++) {
+            const int ch = t + 256 * kq;
+            const int col = ch >> 4, seg = ch & 15;
+            const int64_t c = c0 + col, r = r0 + 16 * seg;
+            if (c >= C || r >= R) continue;
+            const uint8_t* src = &tile[col * CW_STR + 16 * seg];
+            uint8_t* dst = qt + c * ld_qt + r;
+            if (VEC_OUT && r + 16 <= R) {
+                *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+            } else {
+                for (int bb = 0; bb < 16; bb++)
+                    if (r + bb < R) dst[bb] = src[bb];
             }
         }
-    }
-    // Encode along rows: column j of the lane gets the bytes of rows 8*qd .. 8*qd+7.
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-        const uint32_t w0 = enc4<FMT>(y[0][j], y[1][j], y[2][j], y[3][j]);
-        const uint32_t w1 = enc4<FMT>(y[4][j], y[5][j], y[6][j], y[7][j]);
-        *reinterpret_cast<uint2*>(&tile[(8 * o + j) * CW_STR + 8 * qd]) = make_uint2(w0, w1);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-        const int ch = t + 256 * k;
-        const int col = ch >> 4, seg = ch & 15;
-        const int64_t c = c0 + col, r = r0 + 16 * seg;
-        if (c >= C || r >= R) continue;
-        const uint8_t* src = &tile[col * CW_STR + 16 * seg];
-        uint8_t* dst = qt + c * ld_qt + r;
-        if (VEC_OUT && r + 16 <= R) {
-            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
-        } else {
-            for (int b = 0; b < 16; b++)
-                if (r + b < R) dst[b] = src[b];
-        }
+        for (int i = 0; i < 8; i++) v[i] = vn[i];
     }
 }
 
@@ -233,10 +306,15 @@ template <int FMT, bool VEC, bool VEC_OUT>
 static void launch_cast(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x,
                         const int32_t* offsets, int G, const uint32_t* ws, uint8_t* qt,
                         int64_t ld_qt, float* s, hipStream_t stream) {
-    const int64_t rt = R > 0 ? (R + CW_TR - 1) / CW_TR : 1;
+    const int64_t rt = R > 0 ? (R + CW_TR * CW_TPB - 1) / (CW_TR * CW_TPB) : 1;
     const int64_t ct = (C + CW_TC - 1) / CW_TC;
-    colwise_cast_kernel<FMT, VEC, VEC_OUT><<<dim3((unsigned)rt, (unsigned)ct), dim3(256), 0, stream>>>(
-        x, R, C, ld_x, offsets, G, ws, qt, ld_qt, s);
+    const dim3 grid((unsigned)rt, (unsigned)ct);
+    if (G <= CW_GLDS)
+        colwise_cast_kernel<FMT, VEC, VEC_OUT, true><<<grid, dim3(256), 0, stream>>>(
+            x, R, C, ld_x, offsets, G, ws, qt, ld_qt, s);
+    else
+        colwise_cast_kernel<FMT, VEC, VEC_OUT, false><<<grid, dim3(256), 0, stream>>>(
+            x, R, C, ld_x, offsets, G, ws, qt, ld_qt, s);
 }
 
 template <int FMT>
@@ -250,9 +328,17 @@ static fp8q_status_t colwise_run(const uint16_t* x, int64_t R, int64_t C, int64_
     if (zb > 4096) zb = 4096;
     cw_zero_kernel<<<dim3((unsigned)zb), dim3(256), 0, stream>>>(ws, n);
     if (R > 0) {
-        const dim3 grid((unsigned)((R + CW_TR - 1) / CW_TR), (unsigned)((C + CW_TC - 1) / CW_TC));
-        if (vec) colwise_amax_kernel<true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws);
-        else colwise_amax_kernel<false><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws);
+        const dim3 grid((unsigned)((R + CW_TR * CW_TPB - 1) / (CW_TR * CW_TPB)),
+                        (unsigned)((C + CW_TC - 1) / CW_TC));
+        const bool lds = G <= CW_GLDS;
+        if (vec && lds)
+            colwise_amax_kernel<true, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws);
+        else if (vec)
+            colwise_amax_kernel<true, false><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws);
+        else if (lds)
+            colwise_amax_kernel<false, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws);
+        else
+            colwise_amax_kernel<false, false><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws);
     }
     if (vec && vec_out) launch_cast<FMT, true, true>(x, R, C, ld_x, offsets, G, ws, qt, ld_qt, s, stream);
     else if (vec) launch_cast<FMT, true, false>(x, R, C, ld_x, offsets, G, ws, qt, ld_qt, s, stream);

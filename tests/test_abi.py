@@ -85,3 +85,19 @@ def test_argument_errors_are_caught_on_the_host(lib):
     assert g(0, 1, dummy, 16, dummy, dummy, 16, 0, dummy, dummy, 0, 4, 4, 16, dummy, 4, None) == 1
     assert g(1, 1, dummy, 16, dummy, dummy, 16, 16, dummy, dummy, 1, 4, 4, 16, dummy, 4,
              None) == 1  # wgrad needs b_group_stride == 0
+
+
+def test_device_code_has_no_generic_memory_instructions():
+    """Every device access is written against LDS or global memory explicitly (no flat
+    instructions, whose LDS/global routing follows the aperture of the base register)."""
+    from fp8_quantization_grouped_amd import _build
+    srcs = sorted(os.listdir(os.path.join(ROOT, "fp8_quantization_grouped_amd", "csrc")))
+    names = [s[:-4] for s in srcs if s.endswith(".hip")]
+    missing = [n for n in names if not os.path.exists(_build.device_asm(n))]
+    if missing:
+        pytest.skip(f"device assembly not kept for {missing} (run __graft_entry__.build())")
+    for n in names:
+        text = open(_build.device_asm(n)).read()
+        assert "amdgcn" in text
+        hits = _build.FLAT_INSN.findall(text)
+        assert not hits, (n, hits[:4])

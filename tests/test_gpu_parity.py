@@ -139,6 +139,9 @@ COL_CASES = [
     (96, 40, [10, 20, 30, 40, 50, 60, 70, 80, 90, 91, 92, 96]),
     (1, 8, [1]),
     (259, 21, [3, 259]),          # columns not a multiple of 8 -> element-wise path
+    # more groups than the kernels stage in LDS: offsets are read from global memory
+    (4300, 24, sorted(np.random.Generator(np.random.PCG64(11)).integers(0, 4301, 2099).tolist())
+     + [4300]),
 ]
 
 
