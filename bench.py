@@ -50,7 +50,23 @@ def parse():
     ap.add_argument("--workload", default="dsv3", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy 4 times (reference for the HBM "
+                         "byte counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(torch):
+    """A plain device-to-device copy of known size: FETCH_SIZE / WRITE_SIZE of its dispatches
+    give the counters' bytes per algorithmic byte."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 4}), flush=True)
 
 
 def make_inputs(name, torch, dev):
@@ -176,7 +192,7 @@ def cpu_baseline(d, seconds):
     import workloads
     K, N, fmt = d["K"], d["N"], d["fmt"]
     rng_seed = 1234
-    xs = workloads.make_matrix(rng_seed, 256, K, 1.0, 0.0)
+    xs = workloads.make_matrix(rng_seed, 1024, K, 1.0, 0.0)
     ws = workloads.make_matrix(rng_seed + 1, K, N, 0.02)
     t0 = time.perf_counter()
     qa, sa = oracle.quant_rowwise(xs, fmt)
@@ -187,15 +203,45 @@ def cpu_baseline(d, seconds):
     t0 = time.perf_counter()
     oracle.gemm_fwd_rows(fmt, qa, sa, qbt, K, 0, sb, off, N, K, np.arange(4))
     t4 = time.perf_counter() - t0
-    nrows = int(max(4, min(256, 4 * seconds / max(t4, 1e-6))))
+    nrows = int(max(4, min(1024, 4 * seconds / max(t4, 1e-6))))
     t0 = time.perf_counter()
     oracle.gemm_fwd_rows(fmt, qa, sa, qbt, K, 0, sb, off, N, K, np.arange(nrows))
     tg = time.perf_counter() - t0
     return dict(value=2.0 * nrows * N * K / tg / 1e12, unit="TFLOP/s", cores=oracle.num_threads(),
                 kind="oracle",
                 sample=(f"forward grouped GEMM, {nrows} rows x N={N} x K={K} ({tg:.1f} s); "
-                        f"rowwise quant of 256x{K} bf16 at {256 * K * 3 / tq / 1e9:.3f} GB/s"),
-                quant_GBps=256 * K * 3 / tq / 1e9)
+                        f"rowwise quant of 1024x{K} bf16 at {1024 * K * 3 / tq / 1e9:.3f} GB/s"),
+                quant_GBps=1024 * K * 3 / tq / 1e9)
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_dsv3_step.md")
+
+
+def source_hash(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE/WRITE_SIZE summary, or
+    None when there is none or the kernel's source changed since the counters were taken."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    blk = text.split("```json", 1)
+    if len(blk) < 2:
+        return None
+    rec = json.loads(blk[1].split("```", 1)[0])
+    src = ["fp8_quantization_grouped_amd/csrc/grouped_gemm.hip",
+           "fp8_quantization_grouped_amd/csrc/common.hpp"]
+    if rec.get("kernel") != kernel or rec.get("source_sha256_16") != source_hash(src):
+        return None
+    return int(rec["traffic_bytes"])
 
 
 def main():
@@ -206,6 +252,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     import fp8_quantization_grouped_amd as fq
     fq.lib()
     dev = torch.device("cuda:0")
@@ -260,7 +309,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4)}
     roof["kernel"] = dom
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom)
 
     cpu = None
     if not args.no_cpu_baseline:
