@@ -3,9 +3,9 @@
 //
 // FP8 encodings (ai-radar.it "FP8 su GPU AMD ...", section "La correttezza del formato viene
 // prima del tuning": e4m3fnuz, largest value 240, no NaN/Inf code; latestnews.news "AMD Boosts
-// PyTorch FP8 Training on Instinct GPUs", third paragraph: FNUZ = finite, no NaN, unsigned
-// zero).  OCP e4m3fn (largest 448) is the encoding gfx950's conversion and matrix instructions
-// use natively.
+// PyTorch FP8 Training on Instinct GPUs", third paragraph: the FNUZ encoding has only finite
+// codes and one unsigned zero).  OCP e4m3fn (largest 448) is the encoding gfx950's conversion
+// and matrix instructions use natively.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -13,7 +13,8 @@
  *     columnwise outputs are transposed through LDS so that writes coalesce; cross-block
  *     maxima use relaxed-order atomics.
  *   - "AMD Boosts PyTorch FP8 Training on Instinct GPUs" (latestnews.news), third paragraph:
- *     FNUZ is "finite, no NaN, unsigned zero"; grouped GEMM for MoE on ROCm.
+ *     the FNUZ encoding has only finite codes (no NaN/Inf) and a single, unsigned zero;
+ *     grouped GEMM for MoE on ROCm.
  *   - "AMD Primus adds FP8/MXFP8 kernels, megakernel fusion and DeepSeek-V3 training at 1024
  *     GPUs" (fosswire.org), section "What Primus adds for MoE training on MI355X": FP8 and
  *     MXFP8 grouped GEMM for expert FFNs.  MXFP8 itself (1x32 blocks, E8M0 power-of-two
@@ -135,7 +136,11 @@ fp8q_status_t fp8_quant_colwise_grouped(const uint16_t* x, int64_t rows, int64_t
  *   An empty group writes zeros.
  * Accumulation is fp32 on the matrix cores; the result is within 1e-3 + 1e-2*|exact| of the
  * exactly accumulated value for the sizes this library targets.  Element bits of c are not
- * specified beyond that bound. */
+ * specified beyond that bound.
+ * Kernel limits (FP8Q_ERR_UNSUPPORTED, nothing launched): forward needs K, lda, ldb and
+ * b_group_stride multiples of 16; weight gradient needs lda and ldb multiples of 16 (pad the
+ * token dimension; the padding is never read); a and b 16-byte aligned; groups <= 2048;
+ * M, N, K < 2^31 and 256 * lda, 256 * ldb < 2^31. */
 fp8q_status_t fp8_grouped_gemm(fp8q_gemm_mode_t mode, fp8q_format_t fmt, const uint8_t* a,
                                int64_t lda, const float* a_scales, const uint8_t* b,
                                int64_t ldb, int64_t b_group_stride, const float* b_scales,
@@ -169,7 +174,8 @@ fp8q_status_t fp8_mx_quant_colwise(const uint16_t* x, int64_t rows, int64_t cols
  * with ea = a_e8m0[m*ld_sa + kb] - 127, eb_g = b_e8m0[g*sb_group_stride + n*ld_sb + kb] - 127,
  * b_g = b + g*b_group_stride (rows n at stride ldb), K % 32 == 0, e4m3fn elements, fp32
  * accumulation.  Weights from fp8_mx_quant_colwise on [E*K, N]: ldb = E*K,
- * b_group_stride = K, ld_sb = E*K/32, sb_group_stride = K/32. */
+ * b_group_stride = K, ld_sb = E*K/32, sb_group_stride = K/32.
+ * Limits as for the forward FP8 GEMM, plus 256 * ld_sa, 256 * ld_sb < 2^31. */
 fp8q_status_t fp8_mx_grouped_gemm(const uint8_t* a, int64_t lda, const uint8_t* a_e8m0,
                                   int64_t ld_sa, const uint8_t* b, int64_t ldb,
                                   int64_t b_group_stride, const uint8_t* b_e8m0, int64_t ld_sb,
