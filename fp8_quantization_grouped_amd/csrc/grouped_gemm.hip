@@ -186,6 +186,7 @@ __device__ __forceinline__ void group_rows(const GemmArgs& p, int g, int64_t& lo
 
 struct Tile {  // all extents < 2^31 (checked on the host)
     int g, par;  // group; parity of the tile in the block's sequence (scale buffer)
+    int mx_slot;  // MX_DMA: slot of the tile's first 4-step scale chunk
     int row_lo, row_hi, n0, kb_lo, kb_hi, kstart, nk, a_rows, b_rows;
 };
 
@@ -196,14 +197,24 @@ struct Tile {  // all extents < 2^31 (checked on the host)
 // sizes.  Ranges of one XCD are adjacent (blocks are dealt to XCDs round-robin), so concurrent
 // tiles share operand tiles in that XCD's L2.  The first contraction step of a block's next
 // tile is fetched while the current tile finishes.
-template <int FMT, int MODE, bool MX>
+// MX scale loading: none (plain FP8), per-step byte loads (any scale strides), or one 16-byte
+// DMA per row and side every 4 contraction steps (16-byte aligned scale rows).
+constexpr int MX_NONE = 0, MX_BYTES = 1, MX_DMA = 2;
+
+template <int FMT, int MODE, int MXV>
 __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
+    constexpr bool MX = MXV != MX_NONE;
+    // prefix sums: forward counts row-tile slots (< 2^31: M < 2^31, G <= GMAX), wgrad counts
+    // work units (64-bit)
+    typedef typename std::conditional<MODE == MODE_FWD, int, long long>::type pref_t;
     __shared__ __align__(16) uint8_t smem[2][2][STAGE];
-    // MX: 4 E8M0 bytes per row and step (by stage); otherwise the fp32 dequant scales of the
-    // tile's rows [0] and columns [1] (by tile parity)
+    // MX_BYTES: 4 E8M0 bytes per row and step (by stage); otherwise the fp32 dequant scales of
+    // the tile's rows [0] and columns [1] (by tile parity)
     __shared__ __align__(16) uint32_t sscale[2][2][GT];
-    __shared__ long long s_pref[GMAX + 1];                 // per-group prefix of tiles / work
-    __shared__ long long s_part[256];
+    // MX_DMA: E8M0 bytes of 4 steps (16 K blocks) per row: [slot][side][row][16]
+    __shared__ __align__(16) uint8_t smx[MXV == MX_DMA ? 2 * 2 * GT * 16 : 16];
+    __shared__ pref_t s_pref[GMAX + 1];                    // per-group prefix of tiles / work
+    __shared__ pref_t s_part[256];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = wave >> 1, wn = wave & 1;
@@ -212,10 +223,10 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
 
     // --- schedule prefix: forward = row-tile slots per group; wgrad = work units per group
     if (t == 0) s_pref[0] = 0;
-    long long base = 0;
+    pref_t base = 0;
     for (int g0 = 0; g0 < p.G; g0 += 256) {
         const int gg = g0 + t;
-        long long cnt = 0;
+        pref_t cnt = 0;
         if (gg < p.G) {
             int64_t lo, hi;
             group_rows(p, gg, lo, hi);
@@ -231,7 +242,7 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
         s_part[t] = cnt;
         __syncthreads();
         for (int off = 1; off < 256; off <<= 1) {
-            const long long add = t >= off ? s_part[t - off] : 0;
+            const pref_t add = t >= off ? s_part[t - off] : 0;
             __syncthreads();
             s_part[t] += add;
             __syncthreads();
@@ -270,6 +281,7 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
     const long long t_end = first_tile_at(w_hi);
     const long long first_ti = first_tile_at(w_lo) + lb;
     long long ti = first_ti;
+    int mx_next_slot = 0;
     // Returns false when the block's share is exhausted.
     auto next_tile = [&](Tile& T) -> bool {
         if (ti >= t_end) return false;
@@ -307,6 +319,9 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
         ti += bpx;
         T.nk = T.kb_hi > T.kstart ? (T.kb_hi - T.kstart + GK - 1) / GK : 0;
         T.b_rows = p.N - T.n0 < GT ? (int)(p.N - T.n0) : GT;
+        // scale chunks alternate between the two slots across the block's tiles
+        T.mx_slot = mx_next_slot;
+        mx_next_slot = (mx_next_slot + (T.nk + 3) / 4) & 1;
         return true;
     };
 
@@ -347,7 +362,23 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
             dma4(rsm, (uint32_t)t * 4u, lds_addr(&sscale[T.par][0][wave * 64]));
             dma4(rsn, (uint32_t)t * 4u, lds_addr(&sscale[T.par][1][wave * 64]));
         }
-        if (MX) {
+        if (MXV == MX_DMA && ((kpos - T.kstart) / GK) % 4 == 0) {
+            // rows t of both tiles: the 16 E8M0 bytes of this step and the next three (K blocks
+            // kpos/32 .. +15; a scale row is 16-byte aligned and at least that long, blocks past
+            // K are never used)
+            const int slot = (T.mx_slot + (kpos - T.kstart) / (4 * GK)) & 1;
+            const i32x4_t rsa =
+                make_rsrc4(p.a_e8 + (int64_t)T.row_lo * p.ld_sa, (uint32_t)(T.a_rows * p.ld_sa));
+            const i32x4_t rsb =
+                make_rsrc4(p.b_e8 + (int64_t)T.g * p.sbgs + (int64_t)T.n0 * p.ld_sb,
+                           (uint32_t)(T.b_rows * p.ld_sb));
+            const uint32_t kb0 = (uint32_t)(kpos / 32);
+            const uint32_t oa = t < T.a_rows ? (uint32_t)t * (uint32_t)p.ld_sa + kb0 : OOB;
+            const uint32_t ob = t < T.b_rows ? (uint32_t)t * (uint32_t)p.ld_sb + kb0 : OOB;
+            dma16(rsa, oa, lds_addr(&smx[((slot * 2 + 0) * GT + wave * 64) * 16]));
+            dma16(rsb, ob, lds_addr(&smx[((slot * 2 + 1) * GT + wave * 64) * 16]));
+        }
+        if (MXV == MX_BYTES) {
             // rows t of both tiles: the 4 E8M0 bytes of this 128-byte step, packed into one
             // dword per row (blocks past K get 127 = 2^0: their data bytes are zero)
             const __amdgpu_buffer_rsrc_t rsa =
@@ -373,7 +404,7 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
     };
     // MX scales are staged in registers and written to LDS after the step's matrix work.
     auto commit_scales = [&](int stage) {
-        if (MX) {
+        if (MXV == MX_BYTES) {
             sscale[stage][0][t] = sa_pack;
             sscale[stage][1][t] = sb_pack;
         }
@@ -431,20 +462,27 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
             const uint8_t* As = smem[cur_st][0];
             const uint8_t* Bs = smem[cur_st][1];
             const bool kb_in = kpos + 32 * kg < cur.kb_hi;  // MX: this lane's K block exists
+            const int mslot = (cur.mx_slot + (kk >> 2)) & 1, msub = 4 * (kk & 3);
             v8i_t bf[8];
             int sb_[8];
 #pragma unroll
             for (int j = 0; j < 8; j++) {
                 const int rn = wn * 128 + brow(j, lr);
                 bf[j] = frag<true>(Bs, rn, kg, FNUZ);
-                if (MX) sb_[j] = kb_in ? (int)((sscale[cur_st][1][rn] >> (8 * kg)) & 0xFFu) : 127;
+                if (MXV == MX_BYTES)
+                    sb_[j] = kb_in ? (int)((sscale[cur_st][1][rn] >> (8 * kg)) & 0xFFu) : 127;
+                if (MXV == MX_DMA)
+                    sb_[j] = kb_in ? (int)smx[((mslot * 2 + 1) * GT + rn) * 16 + msub + kg] : 127;
             }
 #pragma unroll
             for (int i = 0; i < 8; i++) {
                 const int rm = wm * 128 + i * 16 + lr;
                 const v8i_t af = frag<false>(As, rm, kg, FNUZ);
                 int sa_ = 0;
-                if (MX) sa_ = kb_in ? (int)((sscale[cur_st][0][rm] >> (8 * kg)) & 0xFFu) : 127;
+                if (MXV == MX_BYTES)
+                    sa_ = kb_in ? (int)((sscale[cur_st][0][rm] >> (8 * kg)) & 0xFFu) : 127;
+                if (MXV == MX_DMA)
+                    sa_ = kb_in ? (int)smx[((mslot * 2 + 0) * GT + rm) * 16 + msub + kg] : 127;
 #pragma unroll
                 for (int j = 0; j < 8; j++) {
                     if (MX)
@@ -528,7 +566,7 @@ static int num_cus() {
     return cached[dev];
 }
 
-template <int FMT, int MODE, bool MX>
+template <int FMT, int MODE, int MXV>
 static fp8q_status_t launch_gemm(GemmArgs p, hipStream_t stream) {
     p.nt_n = (int)((p.N + GT - 1) / GT);
     p.nt_k = MODE == MODE_FWD ? 1 : (int)((p.K + GT - 1) / GT);
@@ -541,7 +579,7 @@ static fp8q_status_t launch_gemm(GemmArgs p, hipStream_t stream) {
     if (tiles < grid) grid = tiles;
     if (grid < 1) grid = 1;
     p.vec_store = (p.ldc % 8 == 0) && fp8q_aligned(p.c, 16);
-    gemm256_kernel<FMT, MODE, MX><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p);
+    gemm256_kernel<FMT, MODE, MXV><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p);
     FP8Q_CHECK_LAUNCH();
     return FP8Q_OK;
 }
@@ -573,8 +611,8 @@ extern "C" fp8q_status_t fp8_grouped_gemm(fp8q_gemm_mode_t mode, fp8q_format_t f
         if (K % 16 || lda % 16 || ldb % 16 || b_group_stride % 16 || !fp8q_aligned(a, 16) ||
             !fp8q_aligned(b, 16) || !offsets_fit(lda, ldb))
             return FP8Q_ERR_UNSUPPORTED;
-        if (fmt == FP8Q_E4M3FN) return launch_gemm<FP8Q_E4M3FN, MODE_FWD, false>(p, stream);
-        return launch_gemm<FP8Q_E4M3FNUZ, MODE_FWD, false>(p, stream);
+        if (fmt == FP8Q_E4M3FN) return launch_gemm<FP8Q_E4M3FN, MODE_FWD, MX_NONE>(p, stream);
+        return launch_gemm<FP8Q_E4M3FNUZ, MODE_FWD, MX_NONE>(p, stream);
     }
     if (mode == FP8Q_GEMM_WGRAD_KGROUPED) {
         if (lda < M || ldb < M || b_group_stride != 0) return FP8Q_ERR_INVALID_ARG;
@@ -583,8 +621,8 @@ extern "C" fp8q_status_t fp8_grouped_gemm(fp8q_gemm_mode_t mode, fp8q_format_t f
         if (lda % 16 || ldb % 16 || !fp8q_aligned(a, 16) || !fp8q_aligned(b, 16) ||
             !offsets_fit(lda, ldb))
             return FP8Q_ERR_UNSUPPORTED;
-        if (fmt == FP8Q_E4M3FN) return launch_gemm<FP8Q_E4M3FN, MODE_WGRAD, false>(p, stream);
-        return launch_gemm<FP8Q_E4M3FNUZ, MODE_WGRAD, false>(p, stream);
+        if (fmt == FP8Q_E4M3FN) return launch_gemm<FP8Q_E4M3FN, MODE_WGRAD, MX_NONE>(p, stream);
+        return launch_gemm<FP8Q_E4M3FNUZ, MODE_WGRAD, MX_NONE>(p, stream);
     }
     return FP8Q_ERR_INVALID_ARG;
 }
@@ -610,5 +648,8 @@ extern "C" fp8q_status_t fp8_mx_grouped_gemm(const uint8_t* a, int64_t lda, cons
     p.a = a; p.lda = lda; p.a_e8 = a_e8m0; p.ld_sa = ld_sa; p.b = b; p.ldb = ldb;
     p.bgs = b_group_stride; p.b_e8 = b_e8m0; p.ld_sb = ld_sb; p.sbgs = sb_group_stride;
     p.offsets = offsets; p.G = groups; p.M = M; p.N = N; p.K = K; p.c = c; p.ldc = ldc;
-    return launch_gemm<FP8Q_E4M3FN, MODE_FWD, true>(p, stream);
+    const bool dma = ld_sa % 16 == 0 && ld_sb % 16 == 0 && sb_group_stride % 16 == 0 &&
+                     fp8q_aligned(a_e8m0, 16) && fp8q_aligned(b_e8m0, 16);
+    if (dma) return launch_gemm<FP8Q_E4M3FN, MODE_FWD, MX_DMA>(p, stream);
+    return launch_gemm<FP8Q_E4M3FN, MODE_FWD, MX_BYTES>(p, stream);
 }
