@@ -10,24 +10,25 @@
 //   wgrad, K-grouped:    out[g,k,n] = sum_{m in g} A[k,m] * B[n,m] / (sa[g,k] * sb[g,n])
 //   MX forward:          out[m,n]   = sum_kb 2^(ea+eb) sum_{k in kb} A[m,k] * B_g[n,k]
 //
-// Kernel (one 256-thread block = 4 waves per CU):
+// Kernel (one 256-thread block = 4 waves per CU, persistent: one block per CU):
 //   * 256x256 output tile, 128-byte contraction steps, each wave owns a 128x128 sub-tile
 //     (64 v_mfma_f32_16x16x128_f8f6f4 per step; 256 fp32 accumulators per lane).
 //   * Operand tiles go HBM/L2 -> LDS directly with buffer_load_dwordx4 ... lds (no staging
-//     registers), double-buffered: the loads of step k+1 are issued right after the barrier of
-//     step k and are waited for only after step k's matrix work, so one barrier per step.
-//     Rows and chunks outside the operand are turned into out-of-range buffer offsets and
-//     read back as zeros.  LDS position of (row r, 16-byte chunk c) is r*128 + 16*(c ^ (r&7)),
-//     so the fragment reads (16 rows x one chunk per instruction group) hit distinct banks.
-//   * The MFMA's A operand is the N-side tile and its B operand the M-side tile, so result
-//     register i of lane l is output row l%16, column 4*(l/16)+i: each lane holds four
-//     consecutive outputs of one row and the epilogue stores them as one 8-byte bf16 quad.
-//   * Tiles are numbered so that each XCD (blocks are dealt round-robin to the 8 XCDs) gets a
-//     contiguous run of tiles: the 32 CUs of an XCD share operand tiles in their L2.
+//     registers), double-buffered: after the barrier of step k the loads of step k+1 are
+//     issued in 8 parts between step k's matrix instructions, and waited for only at the top
+//     of step k+1, so one barrier per step.  Rows and chunks outside the operand are turned
+//     into out-of-range buffer offsets and read back as zeros.  Chunks are stored XOR-swizzled
+//     per row (swz, swzB) so that every fragment read is free of LDS bank conflicts.
+//   * The MFMA's A operand is the N-side tile and its B operand the M-side tile; N-side rows
+//     are permuted in LDS (brow) so that each lane ends with 8 consecutive output columns of
+//     one row, stored as one 16-byte bf16 octet.
 //   * Operand lane layout of the 16x16x128 f8f6f4 instruction on gfx950 (established with
 //     one-hot inputs): lane l holds row l%16; its bytes 0-15 are K offsets 16*(l/16)+[0,16) and
 //     bytes 16-31 are K offsets 64+16*(l/16)+[0,16); lane r+16b supplies the E8M0 scale of row
 //     r, K block b.
+//   * Accumulation: the matrix cores add each 32-product block in fixed point whose last bit
+//     is 2^-13 of the block's largest product (products truncated toward zero) and combine
+//     block sums in fp32 (measured on gfx950; the same for the older fp8 instruction).
 //
 // e4m3fnuz operands: the matrix cores read OCP e4m3 only (byte 0x7F, the fnuz 240 code, is NaN
 // there), so fnuz fragments are re-encoded to the e4m3fn byte of the same value after the LDS
@@ -39,10 +40,11 @@
 // first (last) token of the group can carry neighbouring groups' bytes; those bytes of the
 // activation operand are zeroed in LDS on the (at most two) edge steps of a tile.
 //
-// Group scheduling stays on the device (no host read of the offsets): the forward grid covers
-// ceil(M/256) + G row-tile slots per column tile, each block finds its (group, row tile) with a
-// block-wide scan of per-group tile counts, and surplus slots exit.  Offsets are clamped into
-// [0, M] before use, so any offsets content keeps every access in range.
+// Group scheduling stays on the device (no host read of the offsets): each block scans the
+// per-group tile counts (forward) or work units (weight gradient, groups ordered by size,
+// largest first) in LDS, takes an even share of the work for its XCD, and walks its tiles.
+// Offsets are clamped into [0, M] before use, so any offsets content keeps every access in
+// range.
 #include "common.hpp"
 
 namespace fp8q {
@@ -57,10 +59,11 @@ constexpr int STAGE = GT * GK;  // bytes of one operand tile in LDS
 constexpr uint32_t OOB = 0x80000000u;
 constexpr int MODE_FWD = 0, MODE_WGRAD = 1;
 
-// 16-byte slot of chunk c in row r: c ^ (r & 7) ^ ((r >> 3) & 1).  Sixteen consecutive rows
-// at one chunk then land in sixteen distinct 16-byte bank slots (64 x 4-byte banks), and any
-// eight consecutive rows in eight distinct slots (32 banks).
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// 16-byte slot of chunk c in row r: c ^ (2*((r >> 2) & 3) + ((r >> 1) & 1)).  A fragment read
+// is served as two 32-lane halves, each touching 16 consecutive rows at chunks kg ^ s and
+// (kg+1) ^ s; the rows that share a 512-byte LDS window (same r & 3) get distinct
+// 2*((r >> 2) & 3), so all 32 16-byte slots of a half are distinct (no bank conflicts).
+__device__ __forceinline__ int swz(int r) { return (((r >> 2) & 3) << 1) | ((r >> 1) & 1); }
 __device__ __forceinline__ int lds_off(int r, int ch) { return r * GK + ((ch ^ swz(r)) << 4); }
 // N-side tile: its fragments take rows 32j' + 8q + 4h + e (q = lane%16 / 4, e = lane%4) so that
 // each lane's results are 8 consecutive output columns; slot c ^ (2*((r>>3)&3) + ((r>>1)&1))
@@ -176,17 +179,10 @@ struct GemmArgs {
 
 constexpr int GMAX = 2048;  // groups whose schedule prefix fits in LDS
 
-// Group g's token rows, clamped into [0, M] so that any offsets content stays in range.
-__device__ __forceinline__ void group_rows(const GemmArgs& p, int g, int64_t& lo, int64_t& hi) {
-    lo = g == 0 ? 0 : (int64_t)p.offsets[g - 1];
-    lo = lo < 0 ? 0 : (lo > p.M ? p.M : lo);
-    hi = p.offsets[g];
-    hi = hi < lo ? lo : (hi > p.M ? p.M : hi);
-}
-
 struct Tile {  // all extents < 2^31 (checked on the host)
     int g, par;  // group; parity of the tile in the block's sequence (scale buffer)
     int mx_slot;  // MX_DMA: slot of the tile's first 4-step scale chunk
+    int raw_lo, raw_hi;  // the group's offsets as loaded (before clamping)
     int row_lo, row_hi, n0, kb_lo, kb_hi, kstart, nk, a_rows, b_rows;
 };
 
@@ -204,9 +200,12 @@ constexpr int MX_NONE = 0, MX_BYTES = 1, MX_DMA = 2;
 template <int FMT, int MODE, int MXV>
 __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
     constexpr bool MX = MXV != MX_NONE;
-    // prefix sums: forward counts row-tile slots (< 2^31: M < 2^31, G <= GMAX), wgrad counts
-    // work units (64-bit)
-    typedef typename std::conditional<MODE == MODE_FWD, int, long long>::type pref_t;
+    // prefix sums: forward row-tile slots, weight-gradient work units; both < 2^31 (checked
+    // on the host)
+    typedef int pref_t;
+    // group offsets staged in LDS once, except for the MX kernel whose LDS holds the scale
+    // chunks instead (its tiles are long, so the per-tile offsets loads do not matter there)
+    constexpr bool OFF_LDS = MXV != MX_DMA;
     __shared__ __align__(16) uint8_t smem[2][2][STAGE];
     // MX_BYTES: 4 E8M0 bytes per row and step (by stage); otherwise the fp32 dequant scales of
     // the tile's rows [0] and columns [1] (by tile parity)
@@ -214,22 +213,77 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
     // MX_DMA: E8M0 bytes of 4 steps (16 K blocks) per row: [slot][side][row][16]
     __shared__ __align__(16) uint8_t smx[MXV == MX_DMA ? 2 * 2 * GT * 16 : 16];
     __shared__ pref_t s_pref[GMAX + 1];                    // per-group prefix of tiles / work
-    __shared__ pref_t s_part[256];
+    __shared__ int s_off[OFF_LDS ? GMAX : 1];               // offsets as given (unclamped)
+    pref_t* s_part = reinterpret_cast<pref_t*>(&smem[1][0][0]);  // scan scratch (set-up only)
+    // weight gradient: groups in schedule order (most contraction steps first)
+    __shared__ unsigned short s_perm[MODE == MODE_WGRAD ? GMAX : 1];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     constexpr bool FNUZ = FMT == FP8Q_E4M3FNUZ;
     const int64_t tiles_per_group = (int64_t)p.nt_k * p.nt_n;
 
-    // --- schedule prefix: forward = row-tile slots per group; wgrad = work units per group
+    if (OFF_LDS) {
+        for (int i = t; i < p.G; i += 256) s_off[i] = p.offsets[i];
+        __syncthreads();
+    }
+    auto off_at = [&](int g) -> int { return OFF_LDS ? s_off[g] : p.offsets[g]; };
+    // group g's token rows, clamped into [0, M] so that any offsets content stays in range
+    auto rows_of = [&](int g, int64_t& lo, int64_t& hi) {
+        lo = g == 0 ? 0 : (int64_t)off_at(g - 1);
+        lo = lo < 0 ? 0 : (lo > p.M ? p.M : lo);
+        hi = off_at(g);
+        hi = hi < lo ? lo : (hi > p.M ? p.M : hi);
+    };
+    // --- weight gradient: order the groups by contraction steps, largest first, so that the
+    // evenly split ranges end with short tiles (longest-processing-time order); bitonic sort of
+    // (steps, group) keys in the not yet used operand buffer
+    if (MODE == MODE_WGRAD) {
+        long long* key = reinterpret_cast<long long*>(&smem[0][0][0]);  // 16 KB of 32 KB
+        int n = 1;
+        while (n < p.G) n <<= 1;
+        for (int i = t; i < n; i += 256) {
+            long long k = -1;  // padding sorts last
+            if (i < p.G) {
+                int64_t lo, hi;
+                rows_of(i, lo, hi);
+                const int64_t ks = lo & ~(int64_t)15;
+                const int64_t nk = hi > ks ? (hi - ks + GK - 1) / GK : 0;
+                k = ((long long)nk << 11) | (long long)(GMAX - 1 - i);
+            }
+            key[i] = k;
+        }
+        __syncthreads();
+        for (int kb = 2; kb <= n; kb <<= 1) {
+            for (int j = kb >> 1; j > 0; j >>= 1) {
+                for (int i = t; i < n; i += 256) {
+                    const int l = i ^ j;
+                    if (l > i) {
+                        const long long a = key[i], b = key[l];
+                        if ((i & kb) == 0 ? a < b : a > b) {
+                            key[i] = b;
+                            key[l] = a;
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        for (int i = t; i < p.G; i += 256)
+            s_perm[i] = (unsigned short)(GMAX - 1 - (int)(key[i] & (GMAX - 1)));
+        __syncthreads();
+    }
+    auto group_at = [&](int pos) -> int { return MODE == MODE_WGRAD ? (int)s_perm[pos] : pos; };
+
+    // --- forward schedule prefix: row-tile slots per group
     if (t == 0) s_pref[0] = 0;
     pref_t base = 0;
-    for (int g0 = 0; g0 < p.G; g0 += 256) {
+    for (int g0 = 0; MODE == MODE_FWD && g0 < p.G; g0 += 256) {
         const int gg = g0 + t;
         pref_t cnt = 0;
         if (gg < p.G) {
             int64_t lo, hi;
-            group_rows(p, gg, lo, hi);
+            rows_of(group_at(gg), lo, hi);
             if (MODE == MODE_FWD) {
                 cnt = (hi - lo + GT - 1) / GT;
             } else {
@@ -251,108 +305,130 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
         base += s_part[255];
     }
     __syncthreads();
-    const long long total = MODE == MODE_FWD ? s_pref[p.G] * p.nt_n : s_pref[p.G];
-    // The work is split evenly over the XCDs (blocks are dealt to the 8 XCDs round-robin);
-    // inside an XCD's contiguous range the tiles are dealt round-robin to its blocks, so the
-    // tiles running at the same moment are neighbours and share operand tiles in that L2.
+    // Forward: every tile costs the same, so the row-tile slots x column tiles are split evenly
+    // over the XCDs (blocks are dealt to the 8 XCDs round-robin) and dealt round-robin to the
+    // blocks inside each XCD's contiguous range: tiles running at the same moment are
+    // neighbours and share operand tiles in that XCD's L2.
+    // Weight gradient: tiles cost (steps + epilogue) and differ by group, so they are taken in
+    // the size order above, one round of gridDim tiles at a time, alternating the direction
+    // of each round (longest processing time first, snake order).
     const int nb = gridDim.x;
-    const int nx = nb % 8 == 0 ? 8 : 1;
-    const int xcd = nx == 8 ? (int)(blockIdx.x % 8) : 0;
-    const int lb = nx == 8 ? (int)(blockIdx.x / 8) : (int)blockIdx.x;
-    const int bpx = nb / nx;  // blocks per XCD
-    const long long w_lo = total * xcd / nx, w_hi = total * (xcd + 1) / nx;
-    // First tile whose work starts at or after w, as a global tile index (wgrad: tiles are
-    // numbered group by group, tiles_per_group each).
-    auto first_tile_at = [&](long long w) -> long long {
-        if (MODE == MODE_FWD) return w;
-        if (w >= total) return (long long)p.G * tiles_per_group;
-        int lo = 0, hi = p.G - 1;  // last group whose work starts at or before w
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_pref[mid] <= w) lo = mid; else hi = mid - 1;
-        }
-        int64_t glo, ghi;
-        group_rows(p, lo, glo, ghi);
-        const int64_t ks = glo & ~(int64_t)15;
-        const long long unit = (ghi > ks ? (ghi - ks + GK - 1) / GK : 0) + 1;
-        const long long l = (w - s_pref[lo] + unit - 1) / unit;
-        return (long long)lo * tiles_per_group + l;  // may equal the next group's first tile
-    };
-    const long long t_end = first_tile_at(w_hi);
-    const long long first_ti = first_tile_at(w_lo) + lb;
-    long long ti = first_ti;
+    int ti = 0, t_end = 0, bpx = 1, round = 0, par_next = 0;
+    if (MODE == MODE_FWD) {
+        const long long total = (long long)s_pref[p.G] * p.nt_n;  // < 2^31 (host check)
+        const int nx = nb % 8 == 0 ? 8 : 1;
+        const int xcd = nx == 8 ? (int)(blockIdx.x % 8) : 0;
+        const int lb = nx == 8 ? (int)(blockIdx.x / 8) : (int)blockIdx.x;
+        bpx = nb / nx;  // blocks per XCD
+        ti = (int)(total * xcd / nx) + lb;
+        t_end = (int)(total * (xcd + 1) / nx);
+    }
+    const int w_tiles = MODE == MODE_WGRAD ? p.G * (int)tiles_per_group : 0;  // < 2^31 (host)
     int mx_next_slot = 0;
-    // Returns false when the block's share is exhausted.
-    auto next_tile = [&](Tile& T) -> bool {
-        if (ti >= t_end) return false;
+    // The block's next tile, in two halves: tile_start picks the tile and reads its group's
+    // offsets; tile_finish (called later, after other work) derives its extents.  Returns
+    // false when the block's share is exhausted.
+    auto tile_start = [&](Tile& T) -> bool {
         if (MODE == MODE_FWD) {
-            const long long slot = ti / p.nt_n;
-            T.n0 = (int)(ti % p.nt_n) * GT;
+            if (ti >= t_end) return false;
+            const int slot = ti / p.nt_n;
+            T.n0 = (ti % p.nt_n) * GT;
             int lo = 0, hi = p.G - 1;  // last group whose slots start at or before slot
             while (lo < hi) {
                 const int mid = (lo + hi + 1) >> 1;
                 if (s_pref[mid] <= slot) lo = mid; else hi = mid - 1;
             }
             T.g = lo;
-            int64_t glo, ghi;
-            group_rows(p, T.g, glo, ghi);
-            T.row_lo = (int)(glo + (slot - s_pref[T.g]) * GT);
+            T.row_lo = (slot - s_pref[T.g]) * GT;  // relative to the group start
+            ti += bpx;
+        } else {
+            // round r takes tiles [r*nb, r*nb + nb) of the size order; XCD x (blocks are dealt
+            // to the 8 XCDs round-robin) takes one contiguous chunk of them, so the blocks of an
+            // XCD work on neighbouring tiles (shared operand rows in its L2); chunk and position
+            // inside the chunk alternate direction from round to round
+            int idx;
+            if (nb % 8 == 0) {
+                const int cpx = nb / 8, x = (int)blockIdx.x % 8, j = (int)blockIdx.x / 8;
+                const int chunk = (round & 1) ? 7 - x : x;
+                idx = round * nb + chunk * cpx + ((round & 1) ? cpx - 1 - j : j);
+            } else {
+                idx = round * nb + ((round & 1) ? nb - 1 - (int)blockIdx.x : (int)blockIdx.x);
+            }
+            if (idx >= w_tiles) return false;
+            round++;
+            const int tpg = (int)tiles_per_group;
+            T.g = group_at(idx / tpg);
+            const int l = idx % tpg;
+            T.row_lo = (l / p.nt_n) * GT;
+            T.n0 = (l % p.nt_n) * GT;
+        }
+        T.raw_lo = T.g == 0 ? 0 : off_at(T.g - 1);
+        T.raw_hi = off_at(T.g);
+        T.par = par_next;
+        par_next ^= 1;
+        return true;
+    };
+    auto tile_finish = [&](Tile& T) {
+        // the group's token rows, clamped into [0, M] so that any offsets content stays in range
+        int64_t glo = T.raw_lo, ghi = T.raw_hi;
+        glo = glo < 0 ? 0 : (glo > p.M ? p.M : glo);
+        ghi = ghi < glo ? glo : (ghi > p.M ? p.M : ghi);
+        if (MODE == MODE_FWD) {
+            T.row_lo = (int)(glo + T.row_lo);
             T.row_hi = T.row_lo + GT < ghi ? T.row_lo + GT : (int)ghi;
             T.kb_lo = 0;
             T.kb_hi = (int)p.K;
             T.kstart = 0;
             T.a_rows = p.M - T.row_lo < GT ? (int)(p.M - T.row_lo) : GT;
         } else {
-            T.g = (int)(ti / tiles_per_group);
-            const long long l = ti % tiles_per_group;
-            int64_t glo, ghi;
-            group_rows(p, T.g, glo, ghi);
-            T.row_lo = (int)(l / p.nt_n) * GT;
-            T.n0 = (int)(l % p.nt_n) * GT;
             T.row_hi = T.row_lo + GT < p.K ? T.row_lo + GT : (int)p.K;
             T.kb_lo = (int)glo;
             T.kb_hi = (int)ghi;
             T.kstart = (int)(glo & ~(int64_t)15);
             T.a_rows = T.row_hi - T.row_lo;
         }
-        T.par = (int)(((ti - first_ti) / bpx) & 1);
-        ti += bpx;
         T.nk = T.kb_hi > T.kstart ? (T.kb_hi - T.kstart + GK - 1) / GK : 0;
         T.b_rows = p.N - T.n0 < GT ? (int)(p.N - T.n0) : GT;
         // scale chunks alternate between the two slots across the block's tiles
         T.mx_slot = mx_next_slot;
         mx_next_slot = (mx_next_slot + (T.nk + 3) / 4) & 1;
+    };
+    auto next_tile = [&](Tile& T) -> bool {
+        if (!tile_start(T)) return false;
+        tile_finish(T);
         return true;
     };
 
     uint32_t sa_pack = 0, sb_pack = 0;
-    // Step starting at kpos of tile T into LDS stage `stage`: this lane's chunk of each of the
-    // 8 load instructions goes to LDS slot (wave*8+i)*64 + lane.
-    auto issue = [&](const Tile& T, int kpos, int stage) {
-        // Buffer resources rebased at the tile's first rows (offsets stay 32-bit).  Forward
-        // rows of A past row_hi belong to other groups: they are read (finite data) but their
-        // outputs are never stored; only rows past the operand's end are out of range.
-        const i32x4_t ra =
-            make_rsrc4(p.a + (int64_t)T.row_lo * p.lda, (uint32_t)(T.a_rows * p.lda));
-        const i32x4_t rb = make_rsrc4(
+    // A contraction step whose operand loads are still to be issued: buffer resources rebased
+    // at the tile's first rows (offsets stay 32-bit) and the stage's LDS addresses.  Forward
+    // rows of A past row_hi belong to other groups: they are read (finite data) but their
+    // outputs are never stored; only rows past the operand's end are out of range.
+    struct Pend {
+        i32x4_t ra, rb;
+        uint32_t as, bs;
+        int kpos, kb_lo, kb_hi, a_rows, b_rows;
+    };
+    // This lane's row in part i is row0 + 8i (row0 = 64*wave + lane/8); with that row the
+    // swizzles reduce to swz = 4*(i&1) + 2*((lane/32)&1) + ((lane/16)&1) and
+    // swzB = 2*(i&3) + ((lane/16)&1).
+    const int row0 = wave * 64 + (lane >> 3);
+    const int l3 = lane >> 3;
+    // Sets up the step starting at kpos of tile T for LDS stage `stage` and issues the scale
+    // loads that ride along with it.
+    auto prep = [&](const Tile& T, int kpos, int stage) -> Pend {
+        Pend P;
+        P.ra = make_rsrc4(p.a + (int64_t)T.row_lo * p.lda, (uint32_t)(T.a_rows * p.lda));
+        P.rb = make_rsrc4(
             p.b + (MODE == MODE_FWD ? (int64_t)T.g * p.bgs : 0) + (int64_t)T.n0 * p.ldb,
             (uint32_t)(T.b_rows * p.ldb));
-        uint8_t* As = smem[stage][0];
-        uint8_t* Bs = smem[stage][1];
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const int row = (wave * 8 + i) * 8 + (lane >> 3);
-            const int cha = (lane & 7) ^ swz(row), chb = (lane & 7) ^ swzB(row);
-            const int pa = kpos + 16 * cha, pb = kpos + 16 * chb;
-            const bool ka = pa < T.kb_hi && pa + 16 > T.kb_lo;
-            const bool kb = pb < T.kb_hi && pb + 16 > T.kb_lo;
-            const uint32_t aoff =
-                (ka && row < T.a_rows) ? (uint32_t)row * (uint32_t)p.lda + (uint32_t)pa : OOB;
-            const uint32_t boff =
-                (kb && row < T.b_rows) ? (uint32_t)row * (uint32_t)p.ldb + (uint32_t)pb : OOB;
-            dma16(ra, aoff, lds_addr(As + (wave * 8 + i) * 1024));
-            dma16(rb, boff, lds_addr(Bs + (wave * 8 + i) * 1024));
-        }
+        P.as = lds_addr(smem[stage][0]);
+        P.bs = lds_addr(smem[stage][1]);
+        P.kpos = kpos;
+        P.kb_lo = T.kb_lo;
+        P.kb_hi = T.kb_hi;
+        P.a_rows = T.a_rows;
+        P.b_rows = T.b_rows;
         if (!MX && kpos == T.kstart) {
             // the tile's dequant scales (row t of each side) ride along with its first step
             const int64_t sm0 = MODE == MODE_FWD ? (int64_t)T.row_lo : (int64_t)T.g * p.K + T.row_lo;
@@ -401,6 +477,30 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
                 sb_pack |= eb << (8 * j);
             }
         }
+        return P;
+    };
+    // Operand loads of part i of a step: row group (wave*8 + i) of both tiles, 8 rows x 128
+    // bytes per instruction; lane chunk goes to LDS slot (wave*8+i)*64 + lane.
+    auto part = [&](const Pend& P, int i) {
+        const int r = row0, q = l3;
+        const int row = r + 8 * i;
+        const int sa = ((i & 1) << 2) | (((q >> 2) & 1) << 1) | ((q >> 1) & 1);  // swz(row)
+        const int sb = ((i & 3) << 1) | ((q >> 1) & 1);                         // swzB(row)
+        const int cha = (lane & 7) ^ sa, chb = (lane & 7) ^ sb;
+        const int pa = P.kpos + 16 * cha, pb = P.kpos + 16 * chb;
+        const bool ka = pa < P.kb_hi && pa + 16 > P.kb_lo;
+        const bool kb = pb < P.kb_hi && pb + 16 > P.kb_lo;
+        const uint32_t aoff =
+            (ka && row < P.a_rows) ? (uint32_t)row * (uint32_t)p.lda + (uint32_t)pa : OOB;
+        const uint32_t boff =
+            (kb && row < P.b_rows) ? (uint32_t)row * (uint32_t)p.ldb + (uint32_t)pb : OOB;
+        dma16(P.ra, aoff, P.as + (uint32_t)(wave * 8 + i) * 1024u);
+        dma16(P.rb, boff, P.bs + (uint32_t)(wave * 8 + i) * 1024u);
+    };
+    auto issue = [&](const Tile& T, int kpos, int stage) {
+        const Pend P = prep(T, kpos, stage);
+#pragma unroll
+        for (int i = 0; i < 8; i++) part(P, i);
     };
     // MX scales are staged in registers and written to LDS after the step's matrix work.
     auto commit_scales = [&](int stage) {
@@ -449,12 +549,21 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
                 }
             }
             __syncthreads();
+            // the next step's operand loads (this tile's, or the next tile's first) are issued
+            // in 8 parts between this step's matrix instructions
+            // the next tile is looked up on the first step (its offsets loads then have the
+            // whole tile to arrive) and its first step is fetched during the last one
+            if (kk == 0) have_next = tile_start(nxt);
+            Pend P{};
+            bool pend = false;
             if (kk + 1 < cur.nk) {
-                issue(cur, kpos + GK, cur_st ^ 1);
+                P = prep(cur, kpos + GK, cur_st ^ 1);
+                pend = true;
             } else {
-                have_next = next_tile(nxt);
+                if (have_next) tile_finish(nxt);
                 if (have_next && nxt.nk > 0) {
-                    issue(nxt, nxt.kstart, cur_st ^ 1);
+                    P = prep(nxt, nxt.kstart, cur_st ^ 1);
+                    pend = true;
                     next_issued = true;
                 }
             }
@@ -478,6 +587,7 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
             for (int i = 0; i < 8; i++) {
                 const int rm = wm * 128 + i * 16 + lr;
                 const v8i_t af = frag<false>(As, rm, kg, FNUZ);
+                if (pend) part(P, i);
                 int sa_ = 0;
                 if (MXV == MX_BYTES)
                     sa_ = kb_in ? (int)((sscale[cur_st][0][rm] >> (8 * kg)) & 0xFFu) : 127;
@@ -572,6 +682,11 @@ static fp8q_status_t launch_gemm(GemmArgs p, hipStream_t stream) {
     p.nt_k = MODE == MODE_FWD ? 1 : (int)((p.K + GT - 1) / GT);
     if (p.G > GMAX || p.M > 0x7FFFFFFFLL || p.N > 0x7FFFFFFFLL || p.K > 0x7FFFFFFFLL)
         return FP8Q_ERR_UNSUPPORTED;
+    // tile indices are 32-bit: forward row-tile slots (at most one partial per group) times
+    // column tiles, weight-gradient groups times tiles per group
+    const int64_t max_tiles = MODE == MODE_FWD ? ((p.M + GT - 1) / GT + p.G) * p.nt_n
+                                               : (int64_t)p.G * p.nt_k * p.nt_n;
+    if (max_tiles >= 0x7FFFFFFFLL) return FP8Q_ERR_UNSUPPORTED;
     // Upper bound of tiles (forward: each group may add one partial row tile).
     const int64_t tiles = MODE == MODE_FWD ? ((p.M + GT - 1) / GT + p.G) * p.nt_n
                                            : (int64_t)p.G * p.nt_k * p.nt_n;
