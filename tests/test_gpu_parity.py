@@ -142,6 +142,9 @@ COL_CASES = [
     # more groups than the kernels stage in LDS: offsets are read from global memory
     (4300, 24, sorted(np.random.Generator(np.random.PCG64(11)).integers(0, 4301, 2099).tolist())
      + [4300]),
+    # long groups (many row blocks per group and strip), alone and next to short ones
+    (40000, 24, [40000]),
+    (40000, 40, [100, 700, 39000, 40000]),
 ]
 
 
