@@ -15,8 +15,8 @@
 //     (64 v_mfma_f32_16x16x128_f8f6f4 per step; 256 fp32 accumulators per lane).
 //   * Operand tiles go HBM/L2 -> LDS directly with buffer_load_dwordx4 ... lds (no staging
 //     registers), double-buffered: after the barrier of step k the loads of step k+1 are
-//     issued in 8 parts between step k's matrix instructions, and waited for only at the top
-//     of step k+1, so one barrier per step.  Rows and chunks outside the operand are turned
+//     issued in 8 parts between the first half of step k's matrix instructions, and waited for
+//     only at the top of step k+1, so one barrier per step.  Rows and chunks outside the operand are turned
 //     into out-of-range buffer offsets and read back as zeros.  Chunks are stored XOR-swizzled
 //     per row (swz, swzB) so that every fragment read is free of LDS bank conflicts.
 //   * The MFMA's A operand is the N-side tile and its B operand the M-side tile; N-side rows
@@ -550,7 +550,8 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
             }
             __syncthreads();
             // the next step's operand loads (this tile's, or the next tile's first) are issued
-            // in 8 parts between this step's matrix instructions
+            // in 8 parts between the first four rows of this step's matrix instructions, so the
+            // last of them still has half a step to land (MX: between all eight rows)
             // the next tile is looked up on the first step (its offsets loads then have the
             // whole tile to arrive) and its first step is fetched during the last one
             if (kk == 0) have_next = tile_start(nxt);
@@ -587,7 +588,11 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
             for (int i = 0; i < 8; i++) {
                 const int rm = wm * 128 + i * 16 + lr;
                 const v8i_t af = frag<false>(As, rm, kg, FNUZ);
-                if (pend) part(P, i);
+                if (pend && !MX && i < 4) {  // two parts per row in the first half
+                    part(P, 2 * i);
+                    part(P, 2 * i + 1);
+                }
+                if (pend && MX) part(P, i);  // MX: one part per row (measured faster there)
                 int sa_ = 0;
                 if (MXV == MX_BYTES)
                     sa_ = kb_in ? (int)((sscale[cur_st][0][rm] >> (8 * kg)) & 0xFFu) : 127;

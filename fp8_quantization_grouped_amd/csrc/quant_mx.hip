@@ -75,8 +75,8 @@ __global__ __launch_bounds__(256) void mx_colwise_kernel(const uint16_t* __restr
 #pragma unroll
     for (int i = 0; i < 8; i++) {
         const int64_t r = r0 + 8 * qd + i;
-        v[i] = (r < R && c < C) ? *reinterpret_cast<const uint4*>(x + r * ld_x + c)
-                                : make_uint4(0, 0, 0, 0);
+        v[i] = (r < R && c < C) ? ld_nt16(reinterpret_cast<const uint4*>(x + r * ld_x + c))
+                                : make_uint4(0, 0, 0, 0);  // read once: streaming loads
     }
     uint32_t m[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
