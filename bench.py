@@ -3,7 +3,8 @@
 One step = one pass of every hot-path operation over one batch of synthetic input resident in
 HBM:
   forward   rowwise quant of X, per-expert colwise quant of W (transposed), M-grouped FP8 GEMM
-  backward  colwise-grouped transposed quant of X and dY, K-grouped FP8 weight-gradient GEMM
+  backward  colwise-grouped transposed quant of X and dY, K-grouped FP8 weight-gradient GEMM;
+            rowwise quant of dY and of W along N, M-grouped FP8 data-gradient GEMM (dX = dY W^T)
   MXFP8     MX rowwise quant of X, MX colwise quant of W, MX grouped GEMM (forward)
 Default workload: the DeepSeek-V3-shaped local expert slice (32 experts, hidden 7168,
 intermediate 2048, 16384 routed token rows, Zipf(1.1) group sizes), e4m3fn.
@@ -35,7 +36,7 @@ FP8_PEAK_TFLOPS = 5000.0    # MI355X dense FP8 (and MXFP8) matrix throughput
 
 WORKLOADS = {
     # name: (workloads-module config, format, ops)
-    "dsv3": ("dsv3_bwd", 1, ("fwd", "wgrad", "mx")),
+    "dsv3": ("dsv3_bwd", 1, ("fwd", "wgrad", "dgrad", "mx")),
     "dense": ("dense", 1, ("fwd",)),
     "moe16b": ("moe16b", 1, ("fwd",)),
     "tiny": ("tiny", 0, ("fwd", "wgrad")),
@@ -97,7 +98,7 @@ def make_inputs(name, torch, dev):
     w = (torch.randn((E * K, N), generator=gen, device=dev, dtype=torch.float32) * 0.02).to(
         torch.bfloat16)
     dy = None
-    if "wgrad" in ops:
+    if "wgrad" in ops or "dgrad" in ops:
         dy = torch.randn((M, N), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
     return dict(M=M, K=K, N=N, E=E, fmt=fmt, ops=ops, x=x, w=w, dy=dy,
                 offsets=torch.tensor(offsets, dtype=torch.int32, device=dev),
@@ -126,6 +127,10 @@ class Step:
                 dw=e(G, K, N, dt=bf),
                 ws_x=e(max(256, fq.fp8_quant_colwise_grouped_workspace_size(M, K, G))),
                 ws_dy=e(max(256, fq.fp8_quant_colwise_grouped_workspace_size(M, N, G))))
+        if "dgrad" in d["ops"]:
+            # data gradient: dY and W quantized rowwise along N (the contraction), dX bf16 [M, K]
+            self.buf.update(dyq=e(M, N), sdyr=e(M, dt=f32), wqn=e(E * K, N), swk=e(E * K, dt=f32),
+                            dx=e(M, K, dt=bf))
         if "mx" in d["ops"]:
             self.buf.update(mxq=e(M, K), mxe=e(M, K // 32), mxwt=e(N, E * K),
                             mxwe=e(N, E * K // 32), ymx=e(M, N, dt=bf))
@@ -145,6 +150,11 @@ class Step:
             self.gemm_bytes["gemm_wgrad"] = K * M + N * M + G * K * N * 2 + G * K * 4 + G * N * 4
             self.bytes["quant_colwise_xT"] = M * K * 3 + G * K * 4
             self.bytes["quant_colwise_dyT"] = M * N * 3 + G * N * 4
+        if "dgrad" in d["ops"]:
+            self.flops["gemm_dgrad"] = 2.0 * M * N * K
+            self.gemm_bytes["gemm_dgrad"] = M * N + E * K * N + M * K * 2 + M * 4 + E * K * 4
+            self.bytes["quant_rowwise_dy"] = M * N * 3 + M * 4
+            self.bytes["quant_rowwise_w"] = E * K * N * 3 + E * K * 4
         if "mx" in d["ops"]:
             self.flops["gemm_mx"] = 2.0 * M * N * K
             self.gemm_bytes["gemm_mx"] = (M * K + E * N * K + M * N * 2 + M * K // 32
@@ -176,6 +186,18 @@ class Step:
                 ("gemm_wgrad", lambda: fq.fp8_grouped_gemm(
                     fq.GEMM_WGRAD_KGROUPED, fmt, b["xqt"], b["sxg"], b["dyqt"], b["sdyg"],
                     d["offsets"], M, N, K, ldb=self.ldm, c=b["dw"])),
+            ]
+        if "dgrad" in d["ops"]:
+            # dX[m, k] = sum_n dY[m, n] W_g[k, n]: the forward mode with W's [K, N] rows of expert
+            # g as the per-group B operand (contraction over N)
+            seq += [
+                ("quant_rowwise_dy", lambda: fq.fp8_quant_rowwise(d["dy"], fmt, q=b["dyq"],
+                                                                  scales=b["sdyr"])),
+                ("quant_rowwise_w", lambda: fq.fp8_quant_rowwise(d["w"], fmt, q=b["wqn"],
+                                                                 scales=b["swk"])),
+                ("gemm_dgrad", lambda: fq.fp8_grouped_gemm(
+                    fq.GEMM_FWD_MGROUPED, fmt, b["dyq"], b["sdyr"], b["wqn"], b["swk"],
+                    d["offsets"], M, K, N, ldb=N, b_group_stride=K * N, c=b["dx"])),
             ]
         if "mx" in d["ops"]:
             seq += [
@@ -331,7 +353,7 @@ def main():
     cfg = {"workload": {
         "dsv3": "DeepSeek-V3-shaped local expert slice: 32 experts, hidden 7168, intermediate "
                 "2048, 16384 routed token rows (Zipf 1.1 group sizes); FP8 forward + "
-                "weight-gradient + MXFP8 forward",
+                "weight-gradient + data-gradient + MXFP8 forward",
         "dense": "Llama3-8B-style FFN GEMM: M=8192, K=4096, N=14336, G=1; FP8 forward",
         "moe16b": "DeepSeek-MoE-16B-shaped experts: 64 experts, K=2048, N=1408, 49152 routed "
                   "rows (top-6, Zipf 1.1); FP8 forward",

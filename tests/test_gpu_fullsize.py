@@ -211,6 +211,21 @@ def test_gemm_wgrad_full_dsv3(fq, dsv3_bwd):
     check_tol_hw(got, ref, hw, "dsv3 weight gradient")
 
 
+def test_gemm_dgrad_full_dsv3(fq, dsv3_fwd, dsv3_bwd):
+    """dX = dY W^T per group at the dsv3 sizes (the bench's data-gradient launch): dY [16384,
+    2048] and W [32*7168, 2048] quantized rowwise along N, output [16384, 7168]."""
+    d = dsv3_bwd
+    M, K, N, E, off = d["M"], d["K"], d["N"], d["E"], d["offsets"]
+    qa, sa = oracle.quant_rowwise(d["dy"], FN)
+    qb, sb = oracle.quant_rowwise(dsv3_fwd["w"], FN)
+    c = fq.fp8_grouped_gemm(fq.GEMM_FWD_MGROUPED, FN, dev(qa), dev(sa), dev(qb), dev(sb),
+                            dev(off), M, K, N, ldb=N, b_group_stride=K * N)
+    rows = sample_rows(off, M, 64, 29)
+    got = c[torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
+    ref = oracle.gemm_fwd_rows(FN, qa, sa, qb, N, K * N, sb, off, K, N, rows)
+    check_tol(got, ref, "dsv3 data gradient")
+
+
 def test_mx_gemm_full_dsv3(fq, dsv3_fwd):
     d = dsv3_fwd
     M, K, N, E, off = d["M"], d["K"], d["N"], d["E"], d["offsets"]

@@ -251,6 +251,34 @@ def test_gemm_fwd_expert_major_weights(fq, fmt):
     gemm_tol_check(c.float().cpu().numpy(), ref, "fwd expert-major")
 
 
+DGRAD_CASES = [
+    # M (tokens), K (hidden, the output columns), N (intermediate, the contraction), offsets
+    (1024, 256, 512, [485, 524, 774, 1024]),    # the C1 shapes and offsets
+    (600, 200, 144, [0, 250, 250, 600]),         # empty groups, ragged tiles (N: multiple of 16)
+]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("case", DGRAD_CASES)
+def test_gemm_dgrad_parity(fq, fmt, case):
+    """Data gradient dX_g = dY_g W_g^T: dY [M, N] and the weights [E*K, N] quantized rowwise along
+    N (the contraction), then the forward mode with expert g's [K, N] weight rows as B
+    (ldb = N, group stride K*N).  Every output element against the oracle."""
+    M, K, N, off = case
+    off = np.asarray(off, np.int32)
+    E = off.size
+    dy = workloads.make_matrix(700 + M, M, N)
+    w = workloads.make_matrix(701 + M, E * K, N, 0.02)
+    qa, sa = oracle.quant_rowwise(dy, fmt)
+    qb, sb = oracle.quant_rowwise(w, fmt)        # per (e, k) scale over N
+    c = fq.fp8_grouped_gemm(fq.GEMM_FWD_MGROUPED, fmt, torch.from_numpy(qa).to(DEV),
+                            torch.from_numpy(sa).to(DEV), torch.from_numpy(qb).to(DEV),
+                            torch.from_numpy(sb).to(DEV), dev_i32(off), M, K, N, ldb=N,
+                            b_group_stride=K * N)
+    ref = oracle.gemm_fwd_rows(fmt, qa, sa, qb, N, K * N, sb, off, K, N, np.arange(M))
+    gemm_tol_check(c.float().cpu().numpy(), ref, f"dgrad {case}")
+
+
 GEMM_WGRAD_CASES = [
     # M (tokens), K, N, offsets
     (1000, 160, 96, [100, 100, 357, 358, 1000]),
