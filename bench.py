@@ -2,7 +2,8 @@
 
 One step = one pass of every hot-path operation over one batch of synthetic input resident in
 HBM:
-  forward   rowwise quant of X, per-expert colwise quant of W (transposed), M-grouped FP8 GEMM
+  forward   rowwise quant of X, per-expert colwise quant of W (transposed), M-grouped FP8 GEMM;
+            rowwise quant of routed rows gathered in expert order from 2048 token rows (top-8)
   backward  colwise-grouped transposed quant of X and dY, K-grouped FP8 weight-gradient GEMM;
             rowwise quant of dY and of W along N, M-grouped FP8 data-gradient GEMM (dX = dY W^T)
   MXFP8     MX rowwise quant of X, MX colwise quant of W, MX grouped GEMM (forward)
@@ -36,7 +37,7 @@ FP8_PEAK_TFLOPS = 5000.0    # MI355X dense FP8 (and MXFP8) matrix throughput
 
 WORKLOADS = {
     # name: (workloads-module config, format, ops)
-    "dsv3": ("dsv3_bwd", 1, ("fwd", "wgrad", "dgrad", "mx")),
+    "dsv3": ("dsv3_bwd", 1, ("fwd", "gather", "wgrad", "dgrad", "mx")),
     "dense": ("dense", 1, ("fwd",)),
     "moe16b": ("moe16b", 1, ("fwd",)),
     "tiny": ("tiny", 0, ("fwd", "wgrad")),
@@ -127,6 +128,13 @@ class Step:
                 dw=e(G, K, N, dt=bf),
                 ws_x=e(max(256, fq.fp8_quant_colwise_grouped_workspace_size(M, K, G))),
                 ws_dy=e(max(256, fq.fp8_quant_colwise_grouped_workspace_size(M, N, G))))
+        if "gather" in d["ops"]:
+            # dispatch in expert order: 2048 tokens x top-8 over 32 experts (seeded Zipf routing)
+            import workloads
+            _, gidx = workloads.routed_rows_topk(np.random.Generator(np.random.PCG64(6)),
+                                                 M // 8, E, 8)
+            self.gidx = torch.tensor(gidx, device=dev)
+            self.buf.update(gq=e(M, K), gs=e(M, dt=f32))
         if "dgrad" in d["ops"]:
             # data gradient: dY and W quantized rowwise along N (the contraction), dX bf16 [M, K]
             self.buf.update(dyq=e(M, N), sdyr=e(M, dt=f32), wqn=e(E * K, N), swk=e(E * K, dt=f32),
@@ -150,6 +158,9 @@ class Step:
             self.gemm_bytes["gemm_wgrad"] = K * M + N * M + G * K * N * 2 + G * K * 4 + G * N * 4
             self.bytes["quant_colwise_xT"] = M * K * 3 + G * K * 4
             self.bytes["quant_colwise_dyT"] = M * N * 3 + G * N * 4
+        if "gather" in d["ops"]:
+            # minimum traffic: each token row read once, every routed row written, index, scales
+            self.bytes["quant_rowwise_gather_x"] = (M // 8) * K * 2 + M * K + M * 4 + M * 4
         if "dgrad" in d["ops"]:
             self.flops["gemm_dgrad"] = 2.0 * M * N * K
             self.gemm_bytes["gemm_dgrad"] = M * N + E * K * N + M * K * 2 + M * 4 + E * K * 4
@@ -175,6 +186,9 @@ class Step:
                 fq.GEMM_FWD_MGROUPED, fmt, b["xq"], b["sx"], b["wqt"], b["sw"], d["offsets"],
                 M, N, K, ldb=E * K, b_group_stride=K, c=b["y"])),
         ]
+        if "gather" in d["ops"]:
+            seq += [("quant_rowwise_gather_x", lambda: fq.fp8_quant_rowwise_gather(
+                d["x"][: M // 8], self.gidx, fmt, q=b["gq"], scales=b["gs"]))]
         if "wgrad" in d["ops"]:
             seq += [
                 ("quant_colwise_xT", lambda: fq.fp8_quant_colwise_grouped(
@@ -352,8 +366,9 @@ def main():
 
     cfg = {"workload": {
         "dsv3": "DeepSeek-V3-shaped local expert slice: 32 experts, hidden 7168, intermediate "
-                "2048, 16384 routed token rows (Zipf 1.1 group sizes); FP8 forward + "
-                "weight-gradient + data-gradient + MXFP8 forward",
+                "2048, 16384 routed token rows (Zipf 1.1 group sizes); FP8 forward (+ rowwise "
+                "quant gathered in expert order from 2048 tokens x top-8) + weight-gradient + "
+                "data-gradient + MXFP8 forward",
         "dense": "Llama3-8B-style FFN GEMM: M=8192, K=4096, N=14336, G=1; FP8 forward",
         "moe16b": "DeepSeek-MoE-16B-shaped experts: 64 experts, K=2048, N=1408, 49152 routed "
                   "rows (top-6, Zipf 1.1); FP8 forward",

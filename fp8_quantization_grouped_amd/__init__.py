@@ -32,6 +32,7 @@ SIGNATURES = {
     "fp8q_abi_version": (_I, []),
     "fp8q_status_string": (ctypes.c_char_p, [_I]),
     "fp8_quant_rowwise": (_I, [_P, _I64, _I64, _I64, _I, _P, _I64, _P, _P]),
+    "fp8_quant_rowwise_gather": (_I, [_P, _I64, _I64, _I64, _P, _I64, _I, _P, _I64, _P, _P]),
     "fp8_quant_colwise_grouped_workspace_size": (_SZ, [_I64, _I64, _I32]),
     "fp8_quant_colwise_grouped": (_I, [_P, _I64, _I64, _I64, _P, _I32, _I, _P, _I64, _P, _P, _SZ,
                                        _P]),
@@ -93,6 +94,27 @@ def fp8_quant_rowwise(x: torch.Tensor, fmt: int, q: torch.Tensor | None = None,
     st = lib().fp8_quant_rowwise(_ptr(x), rows, cols, x.stride(0), fmt, _ptr(q), q.stride(0),
                                  _ptr(scales), _stream(x))
     _check("fp8_quant_rowwise", st)
+    return q, scales
+
+
+def fp8_quant_rowwise_gather(x: torch.Tensor, row_index: torch.Tensor, fmt: int,
+                             q: torch.Tensor | None = None, scales: torch.Tensor | None = None):
+    """Rowwise quantization of the rows x[row_index[r]] (indices clamped into range).
+    x: bf16 [src_rows, cols]; row_index: int32 [rows] on the device.  Returns (q uint8
+    [rows, cols], scales float32 [rows])."""
+    _dev(x, "x")
+    _dev(row_index, "row_index")
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    assert row_index.dtype == torch.int32 and row_index.dim() == 1 and row_index.is_contiguous()
+    src_rows, cols = x.shape
+    rows = row_index.numel()
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    st = lib().fp8_quant_rowwise_gather(_ptr(x), src_rows, cols, x.stride(0), _ptr(row_index),
+                                        rows, fmt, _ptr(q), q.stride(0), _ptr(scales), _stream(x))
+    _check("fp8_quant_rowwise_gather", st)
     return q, scales
 
 

@@ -9,16 +9,32 @@
 // then scaled, clamped and converted with v_cvt_pk_fp8_f32 and stored 8 bytes per lane
 // (consecutive lanes -> consecutive addresses).  HBM traffic is the algorithmic minimum:
 // 2 bytes read + 1 byte written per element + 4 bytes per row scale.
+//
+// Gathered variant (fosswire.org "AMD Primus adds FP8/MXFP8 kernels ...", section "What Primus
+// adds for MoE training on MI355X": the MegaMoE item fuses the token exchange with the kernels
+// that consume its rows): output row r quantizes source row index[r], so routed token rows are
+// put into expert order and quantized in the same pass, with no permuted bf16 copy in HBM.  The
+// index is read once per row (wave-uniform, a scalar load) and clamped into the source rows.
 #include "common.hpp"
 
 namespace fp8q {
+
+// Source row of output row `row`: the identity, or index[row] clamped into [0, src_rows).
+__device__ __forceinline__ int64_t src_row(const int32_t* __restrict__ index, int64_t src_rows,
+                                           int64_t row) {
+    if (!index) return row;
+    const int64_t r = (int64_t)index[row];
+    return r < 0 ? 0 : (r >= src_rows ? src_rows - 1 : r);
+}
 
 template <int FMT, int WPR, int NV>
 __global__ __launch_bounds__(256) void rowwise_vec_kernel(const uint16_t* __restrict__ x,
                                                           int64_t rows, int64_t cols,
                                                           int64_t ld_x, uint8_t* __restrict__ q,
                                                           int64_t ld_q,
-                                                          float* __restrict__ scales) {
+                                                          float* __restrict__ scales,
+                                                          const int32_t* __restrict__ index,
+                                                          int64_t src_rows) {
     constexpr int RPB = 4 / WPR;   // rows per 256-thread block
     constexpr int TPR = 64 * WPR;  // threads per row
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -26,7 +42,8 @@ __global__ __launch_bounds__(256) void rowwise_vec_kernel(const uint16_t* __rest
     const int t = (wave % WPR) * 64 + lane;
     const bool row_ok = row < rows;
     const int64_t nchunks = cols >> 3;
-    const uint4* xr = reinterpret_cast<const uint4*>(x + (row_ok ? row : 0) * ld_x);
+    const int64_t sr = row_ok ? src_row(index, src_rows, row) : 0;
+    const uint4* xr = reinterpret_cast<const uint4*>(x + sr * ld_x);
 
     uint4 v[NV];
     uint32_t m = 0;
@@ -34,7 +51,8 @@ __global__ __launch_bounds__(256) void rowwise_vec_kernel(const uint16_t* __rest
     for (int j = 0; j < NV; j++) {
         const int64_t c = t + (int64_t)j * TPR;
         if (row_ok && c < nchunks) {
-            v[j] = ld_nt16(xr + c);
+            // streaming loads when each row is read once; a gather may read a row repeatedly
+            v[j] = index ? xr[c] : ld_nt16(xr + c);
         } else {
             v[j] = make_uint4(0, 0, 0, 0);
         }
@@ -76,9 +94,11 @@ __global__ __launch_bounds__(256) void rowwise_generic_kernel(const uint16_t* __
                                                               int64_t cols, int64_t ld_x,
                                                               uint8_t* __restrict__ q,
                                                               int64_t ld_q,
-                                                              float* __restrict__ scales) {
+                                                              float* __restrict__ scales,
+                                                              const int32_t* __restrict__ index,
+                                                              int64_t src_rows) {
     const int64_t row = blockIdx.x;
-    const uint16_t* xr = x + row * ld_x;
+    const uint16_t* xr = x + src_row(index, src_rows, row) * ld_x;
     uint32_t m = 0;
     for (int64_t c = threadIdx.x; c < cols; c += 256) {
         uint32_t a = xr[c] & 0x7FFFu;
@@ -102,29 +122,33 @@ __global__ __launch_bounds__(256) void rowwise_generic_kernel(const uint16_t* __
 
 template <int FMT, int WPR, int NV>
 static void launch_vec(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
-                       int64_t ld_q, float* s, hipStream_t stream) {
+                       int64_t ld_q, float* s, const int32_t* index, int64_t src_rows,
+                       hipStream_t stream) {
     constexpr int RPB = 4 / WPR;
     const int64_t blocks = (rows + RPB - 1) / RPB;
     rowwise_vec_kernel<FMT, WPR, NV><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
-        x, rows, cols, ld_x, q, ld_q, s);
+        x, rows, cols, ld_x, q, ld_q, s, index, src_rows);
 }
 
 template <int FMT>
 static fp8q_status_t rowwise_dispatch(const uint16_t* x, int64_t rows, int64_t cols,
                                       int64_t ld_x, uint8_t* q, int64_t ld_q, float* s,
+                                      const int32_t* index, int64_t src_rows,
                                       hipStream_t stream) {
     const bool vec = (cols % 8 == 0) && (ld_x % 8 == 0) && (ld_q % 8 == 0) &&
                      fp8q_aligned(x, 16) && fp8q_aligned(q, 8);
-    if (vec && cols <= 512) launch_vec<FMT, 1, 1>(x, rows, cols, ld_x, q, ld_q, s, stream);
-    else if (vec && cols <= 1024) launch_vec<FMT, 1, 2>(x, rows, cols, ld_x, q, ld_q, s, stream);
-    else if (vec && cols <= 2048) launch_vec<FMT, 1, 4>(x, rows, cols, ld_x, q, ld_q, s, stream);
-    else if (vec && cols <= 4096) launch_vec<FMT, 1, 8>(x, rows, cols, ld_x, q, ld_q, s, stream);
-    else if (vec && cols <= 8192) launch_vec<FMT, 2, 8>(x, rows, cols, ld_x, q, ld_q, s, stream);
-    else if (vec && cols <= 16384) launch_vec<FMT, 4, 8>(x, rows, cols, ld_x, q, ld_q, s, stream);
-    else if (vec && cols <= 32768) launch_vec<FMT, 4, 16>(x, rows, cols, ld_x, q, ld_q, s, stream);
+#define RW(WPR, NV) launch_vec<FMT, WPR, NV>(x, rows, cols, ld_x, q, ld_q, s, index, src_rows, stream)
+    if (vec && cols <= 512) RW(1, 1);
+    else if (vec && cols <= 1024) RW(1, 2);
+    else if (vec && cols <= 2048) RW(1, 4);
+    else if (vec && cols <= 4096) RW(1, 8);
+    else if (vec && cols <= 8192) RW(2, 8);
+    else if (vec && cols <= 16384) RW(4, 8);
+    else if (vec && cols <= 32768) RW(4, 16);
     else
         rowwise_generic_kernel<FMT><<<dim3((unsigned)rows), dim3(256), 0, stream>>>(
-            x, cols, ld_x, q, ld_q, s);
+            x, cols, ld_x, q, ld_q, s, index, src_rows);
+#undef RW
     FP8Q_CHECK_LAUNCH();
     return FP8Q_OK;
 }
@@ -140,6 +164,26 @@ extern "C" fp8q_status_t fp8_quant_rowwise(const uint16_t* x, int64_t rows, int6
     if (!scales || (cols > 0 && (!x || !q))) return FP8Q_ERR_INVALID_ARG;
     if (rows > 0x7FFFFFFFLL) return FP8Q_ERR_UNSUPPORTED;
     if (fmt == FP8Q_E4M3FN)
-        return fp8q::rowwise_dispatch<FP8Q_E4M3FN>(x, rows, cols, ld_x, q, ld_q, scales, stream);
-    return fp8q::rowwise_dispatch<FP8Q_E4M3FNUZ>(x, rows, cols, ld_x, q, ld_q, scales, stream);
+        return fp8q::rowwise_dispatch<FP8Q_E4M3FN>(x, rows, cols, ld_x, q, ld_q, scales, nullptr,
+                                                   rows, stream);
+    return fp8q::rowwise_dispatch<FP8Q_E4M3FNUZ>(x, rows, cols, ld_x, q, ld_q, scales, nullptr,
+                                                 rows, stream);
+}
+
+extern "C" fp8q_status_t fp8_quant_rowwise_gather(const uint16_t* x, int64_t src_rows,
+                                                  int64_t cols, int64_t ld_x,
+                                                  const int32_t* row_index, int64_t rows,
+                                                  fp8q_format_t fmt, uint8_t* q, int64_t ld_q,
+                                                  float* scales, hipStream_t stream) {
+    if (rows < 0 || src_rows < 0 || cols < 0 || ld_x < cols || ld_q < cols || !fp8q_fmt_ok(fmt))
+        return FP8Q_ERR_INVALID_ARG;
+    if (rows == 0) return FP8Q_OK;
+    if (src_rows == 0 || !row_index || !scales || (cols > 0 && (!x || !q)))
+        return FP8Q_ERR_INVALID_ARG;
+    if (rows > 0x7FFFFFFFLL) return FP8Q_ERR_UNSUPPORTED;
+    if (fmt == FP8Q_E4M3FN)
+        return fp8q::rowwise_dispatch<FP8Q_E4M3FN>(x, rows, cols, ld_x, q, ld_q, scales,
+                                                   row_index, src_rows, stream);
+    return fp8q::rowwise_dispatch<FP8Q_E4M3FNUZ>(x, rows, cols, ld_x, q, ld_q, scales,
+                                                 row_index, src_rows, stream);
 }

@@ -84,6 +84,22 @@ fp8q_status_t fp8_quant_rowwise(const uint16_t* x, int64_t rows, int64_t cols, i
                                 fp8q_format_t fmt, uint8_t* q, int64_t ld_q, float* scales,
                                 hipStream_t stream);
 
+/* Rowwise quantization of gathered rows (fosswire.org "AMD Primus adds FP8/MXFP8 kernels ...",
+ * section "What Primus adds for MoE training on MI355X": the MegaMoE item fuses the token
+ * exchange with the kernels that consume its rows; here the one-GPU half, routed token rows put
+ * into expert order and quantized in one pass).  For r in [0, rows):
+ *   q[r*ld_q + k] and scales[r] = fp8_quant_rowwise of source row i = row_index[r],
+ * with i clamped into [0, src_rows) (an out-of-range index reads the nearest end row; it is
+ * never an out-of-bounds access).  A source row may be listed any number of times.
+ *   x          bf16 [src_rows][ld_x], ld_x >= cols
+ *   row_index  int32 [rows] device
+ *   q          u8   [rows][ld_q], ld_q >= cols;  scales fp32 [rows]
+ * rows == 0 is a no-op; src_rows == 0 with rows > 0 is FP8Q_ERR_INVALID_ARG. */
+fp8q_status_t fp8_quant_rowwise_gather(const uint16_t* x, int64_t src_rows, int64_t cols,
+                                       int64_t ld_x, const int32_t* row_index, int64_t rows,
+                                       fp8q_format_t fmt, uint8_t* q, int64_t ld_q,
+                                       float* scales, hipStream_t stream);
+
 /* Bytes of device workspace fp8_quant_colwise_grouped needs (its cross-block maxima). */
 size_t fp8_quant_colwise_grouped_workspace_size(int64_t rows, int64_t cols, int32_t groups);
 

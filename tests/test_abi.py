@@ -26,7 +26,8 @@ def declared_functions():
 
 def test_header_declares_the_hot_path():
     names = declared_functions()
-    for must in ("fp8_quant_rowwise", "fp8_quant_colwise_grouped", "fp8_grouped_gemm",
+    for must in ("fp8_quant_rowwise", "fp8_quant_rowwise_gather", "fp8_quant_colwise_grouped",
+                 "fp8_grouped_gemm",
                  "fp8_mx_quant_rowwise", "fp8_mx_quant_colwise", "fp8_mx_grouped_gemm",
                  "fp8_quant_colwise_grouped_workspace_size", "fp8q_status_string",
                  "fp8q_abi_version"):
@@ -78,6 +79,13 @@ def test_argument_errors_are_caught_on_the_host(lib):
     assert f(dummy, 4, 8, 4, 1, dummy, 8, dummy, None) == 1
     assert f(dummy, 4, 8, 8, 2, dummy, 8, dummy, None) == 1
     assert f(dummy, 0, 8, 8, 1, dummy, 8, dummy, None) == 0  # empty: no-op
+    gq = lib.fp8_quant_rowwise_gather
+    gq.restype = I
+    gq.argtypes = [P, I64, I64, I64, P, I64, I, P, I64, P, P]
+    assert gq(dummy, 0, 8, 8, dummy, 4, 1, dummy, 8, dummy, None) == 1   # no source rows
+    assert gq(dummy, 4, 8, 8, None, 4, 1, dummy, 8, dummy, None) == 1    # no index
+    assert gq(dummy, 4, 8, 8, dummy, -1, 1, dummy, 8, dummy, None) == 1
+    assert gq(dummy, 0, 8, 8, None, 0, 1, dummy, 8, dummy, None) == 0    # empty: no-op
     g = lib.fp8_grouped_gemm
     g.restype = I
     g.argtypes = [I, I, P, I64, P, P, I64, I64, P, P, ctypes.c_int32, I64, I64, I64, P, I64, P]

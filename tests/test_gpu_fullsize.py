@@ -123,6 +123,17 @@ def test_rowwise_full_dsv3_activations(fq, dsv3_fwd, fmt):
     assert np.array_equal(q.cpu().numpy(), oq)
 
 
+def test_rowwise_gather_full_dsv3(fq, dsv3_fwd):
+    """2048 tokens x top-8 routed to 32 experts (Zipf): the 16384 expert-ordered rows of hidden
+    7168 quantized straight from the token activations."""
+    x = dsv3_fwd["x"][:2048]
+    _, idx = workloads.routed_rows_topk(np.random.Generator(np.random.PCG64(6)), 2048, 32, 8)
+    q, s = fq.fp8_quant_rowwise_gather(workloads.to_torch_bf16(x, DEV), dev(idx), FN)
+    oq, os_ = oracle.quant_rowwise(x[idx], FN)
+    assert np.array_equal(s.cpu().numpy(), os_)
+    assert np.array_equal(q.cpu().numpy(), oq)
+
+
 def test_colwise_full_dsv3_weights(fq, dsv3_fwd):
     d = dsv3_fwd
     E, K = d["E"], d["K"]

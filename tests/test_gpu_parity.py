@@ -128,6 +128,38 @@ def test_rowwise_padded_leading_dims(fq, fmt):
     assert np.all(qb[:, cols:] == 0xAB)  # nothing written past the row
 
 
+GATHER_CASES = [
+    # tokens, cols, topk, ld_x pad
+    (256, 256, 4, 0),      # the C1 width, 1024 routed rows
+    (300, 6144, 2, 64),    # wider rows (two waves per row), padded source stride
+    (50, 100, 3, 0),       # columns not a multiple of 8: element-wise path
+]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("case", GATHER_CASES)
+def test_rowwise_gather_parity(fq, fmt, case):
+    """Routed token rows quantized in expert order: bytes and scales equal the oracle's rowwise
+    quantization of x[index] (numpy gather), repeated source rows included."""
+    tokens, cols, topk, pad = case
+    x = workloads.make_matrix(900 + tokens, tokens, cols, 1.0, 0.01)
+    _, idx = workloads.routed_rows_topk(np.random.Generator(np.random.PCG64(tokens)), tokens,
+                                        8, topk)
+    q, sc = fq.fp8_quant_rowwise_gather(dev_bf16(x, ld=cols + pad), dev_i32(idx), fmt)
+    oq, os_ = oracle.quant_rowwise(x[idx], fmt)
+    assert np.array_equal(sc.cpu().numpy(), os_)
+    assert np.array_equal(q.cpu().numpy(), oq)
+
+
+def test_rowwise_gather_index_clamped(fq):
+    """Out-of-range indices read the nearest end row (never out of bounds)."""
+    x = workloads.make_matrix(77, 20, 64, 2.0)
+    idx = np.array([5, -3, 19, 20, 1000, 0, -2147483648, 2147483647], np.int32)
+    q, sc = fq.fp8_quant_rowwise_gather(dev_bf16(x), dev_i32(idx), FN)
+    oq, os_ = oracle.quant_rowwise(x[np.clip(idx, 0, 19)], FN)
+    assert np.array_equal(sc.cpu().numpy(), os_) and np.array_equal(q.cpu().numpy(), oq)
+
+
 # ----------------------------------------------------------------------------- colwise
 
 COL_CASES = [

@@ -94,6 +94,21 @@ def routed_offsets_topk(rng: np.random.Generator, tokens: int, experts: int, top
     return offsets_from_sizes(counts)
 
 
+def routed_rows_topk(rng: np.random.Generator, tokens: int, experts: int, topk: int,
+                     s: float = 1.1):
+    """Token dispatch in expert order: each token picks topk distinct experts (Gumbel-top-k over
+    log Zipf weights); rows are sorted by expert, tokens ascending inside an expert.  Returns
+    (offsets int32 [experts], index int32 [tokens*topk]: the source token of each row)."""
+    logp = np.log(zipf_probs(rng, experts, s))
+    g = rng.gumbel(size=(tokens, experts))
+    top = np.argpartition(-(logp[None, :] + g), topk - 1, axis=1)[:, :topk]   # [tokens, topk]
+    expert = top.ravel()
+    token = np.repeat(np.arange(tokens, dtype=np.int64), topk)
+    order = np.lexsort((token, expert))
+    counts = np.bincount(expert, minlength=experts)
+    return offsets_from_sizes(counts), token[order].astype(np.int32)
+
+
 def multinomial_offsets(rng: np.random.Generator, rows: int, experts: int, s: float = 1.1) -> np.ndarray:
     p = zipf_probs(rng, experts, s)
     return offsets_from_sizes(rng.multinomial(rows, p))
