@@ -74,6 +74,9 @@ def _load():
     lib.or_mx_gemm_fwd_rows.restype = None
     lib.or_mx_gemm_fwd_rows.argtypes = [P, I64, P, I64, P, I64, I64, P, I64, I64, P, I32, I64,
                                         I64, P, I64, P]
+    lib.or_mx_gemm_wgrad_rows.restype = None
+    lib.or_mx_gemm_wgrad_rows.argtypes = [P, I64, P, I64, P, I64, P, I64, P, I32, I64, P, P, I64,
+                                          P]
     lib.or_num_threads.restype = ctypes.c_int
     lib.or_num_threads.argtypes = []
     _lib = lib
@@ -214,4 +217,22 @@ def mx_gemm_fwd_rows(a, ae8, b, ldb, b_gs, be8, ld_sb, bs_gs, offsets, N, K, row
     _load().or_mx_gemm_fwd_rows(_p(a), a.shape[1], _p(ae8), ae8.shape[1], _p(b), ldb, b_gs,
                                 _p(be8), ld_sb, bs_gs, _p(off), off.shape[0], N, K, _p(idx),
                                 idx.shape[0], _p(out))
+    return out
+
+
+def mx_gemm_wgrad_rows(xt, xe8, dyt, de8, offsets, N, g_idx, k_idx):
+    """MX weight-gradient rows dW[g, k, :] for the listed (g, k); float64 [len, N].  xt: uint8
+    [K, ldx] with xe8 [K, ld_sx] (E8M0 per 32 absolute tokens); dyt: [N, ldd] with de8 [N, ld_sd].
+    Each group sums its own tokens; a 32-token block shared by two groups keeps its scale."""
+    xt = _c(xt, np.uint8)
+    xe8 = _c(xe8, np.uint8)
+    dyt = _c(dyt, np.uint8)
+    de8 = _c(de8, np.uint8)
+    off = _c(offsets, np.int32)
+    gi = _c(g_idx, np.int32)
+    ki = _c(k_idx, np.int64)
+    out = np.zeros((gi.shape[0], N), np.float64)
+    _load().or_mx_gemm_wgrad_rows(_p(xt), xt.shape[1], _p(xe8), xe8.shape[1], _p(dyt),
+                                  dyt.shape[1], _p(de8), de8.shape[1], _p(off), off.shape[0], N,
+                                  _p(gi), _p(ki), gi.shape[0], _p(out))
     return out

@@ -341,6 +341,38 @@ void or_mx_gemm_fwd_rows(const uint8_t* a, int64_t lda, const uint8_t* ae8, int6
     }
 }
 
+/* MX grouped GEMM, weight gradient (K-grouped): the token dimension is the contraction, in 1x32
+ * blocks of absolute token rows (the blocks fp8_mx_quant_colwise forms over all M rows).  A block
+ * that straddles a group boundary keeps its one scale; each group sums only its own tokens:
+ *   out[i*N + n] = sum_{m in g} dec(xt[k,m]) 2^(ex[k, m/32] - 127) dec(dyt[n,m]) 2^(ed[n, m/32] - 127)
+ * for (g, k) = (g_idx[i], k_idx[i]).  Products are summed exactly per block, then scaled. */
+void or_mx_gemm_wgrad_rows(const uint8_t* xt, int64_t ldx, const uint8_t* xe8, int64_t ld_sx,
+                           const uint8_t* dyt, int64_t ldd, const uint8_t* de8, int64_t ld_sd,
+                           const int32_t* offsets, int32_t groups, int64_t N,
+                           const int32_t* g_idx, const int64_t* k_idx, int64_t nrows,
+                           double* out) {
+    (void)groups;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < nrows; i++) {
+        int32_t g = g_idx[i];
+        int64_t k = k_idx[i];
+        int64_t m0 = g == 0 ? 0 : offsets[g - 1], m1 = offsets[g];
+        for (int64_t n = 0; n < N; n++) {
+            double acc = 0.0;
+            int64_t m = m0;
+            while (m < m1) {
+                int64_t blk = m / 32, stop = (blk + 1) * 32 < m1 ? (blk + 1) * 32 : m1;
+                double part = 0.0;
+                for (; m < stop; m++)
+                    part += or_decode(OR_FN, xt[k * ldx + m]) * or_decode(OR_FN, dyt[n * ldd + m]);
+                int ex = (int)xe8[k * ld_sx + blk] - 127, ed = (int)de8[n * ld_sd + blk] - 127;
+                acc += ldexp(part, ex + ed);
+            }
+            out[i * N + n] = acc;
+        }
+    }
+}
+
 /* Threads OpenMP will use (reported next to CPU timings). */
 #ifdef _OPENMP
 #include <omp.h>

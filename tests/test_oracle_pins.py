@@ -453,3 +453,56 @@ def test_mx_gemm_exact_block_sums():
                     tot += Fraction(s) * (Fraction(2) ** e)
                 assert abs(Fraction(out[m - 0, n]) - tot) <= abs(tot) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 300)
         start = end
+
+
+def _mx_wgrad_operands(M, K, N, seed):
+    """XqT, dYqT and their E8M0 bytes from the MX colwise oracle (blocks of 32 tokens)."""
+    x = workloads.make_matrix(seed, M, K, 1.0, 0.01)
+    dy = workloads.make_matrix(seed + 1, M, N)
+    xt, xe = oracle.mx_quant_colwise(x)      # [K, M], [K, M/32]
+    dyt, de = oracle.mx_quant_colwise(dy)    # [N, M], [N, M/32]
+    return xt, xe, dyt, de
+
+
+def test_mx_wgrad_unit_scales_equal_plain_wgrad():
+    """With every E8M0 byte 127 (2^0) the MX weight gradient is the plain FP8 one with unit
+    scales (a separately pinned oracle function)."""
+    M, K, N = 96, 40, 24
+    off = np.array([10, 10, 61, 96], np.int32)
+    xt, _, dyt, _ = _mx_wgrad_operands(M, K, N, 61)
+    ones_x = np.full((K, M // 32), 127, np.uint8)
+    ones_d = np.full((N, M // 32), 127, np.uint8)
+    gi = np.repeat(np.arange(4, dtype=np.int32), K)
+    ki = np.tile(np.arange(K, dtype=np.int64), 4)
+    got = oracle.mx_gemm_wgrad_rows(xt, ones_x, dyt, ones_d, off, N, gi, ki)
+    ref = oracle.gemm_wgrad_rows(FN, xt, np.ones((4, K), np.float32), dyt,
+                                 np.ones((4, N), np.float32), off, N, K, gi, ki)
+    assert np.array_equal(got, ref)
+    assert np.all(got[gi == 1] == 0.0)  # the empty group
+
+
+def test_mx_wgrad_single_group_is_mx_forward_over_tokens():
+    """One group holding every token: dW[k, n] is the MX forward GEMM of the rows of XqT against
+    the rows of dYqT, contracting over tokens (the separately pinned MX forward oracle)."""
+    M, K, N = 128, 24, 20
+    xt, xe, dyt, de = _mx_wgrad_operands(M, K, N, 63)
+    got = oracle.mx_gemm_wgrad_rows(xt, xe, dyt, de, np.array([M], np.int32), N,
+                                    np.zeros(K, np.int32), np.arange(K, dtype=np.int64))
+    ref = oracle.mx_gemm_fwd_rows(xt, xe, dyt, M, 0, de, M // 32, 0, np.array([K], np.int32), N,
+                                  M, np.arange(K))
+    assert np.array_equal(got, ref)
+
+
+def test_mx_wgrad_split_inside_a_block_is_additive():
+    """Splitting a group inside a 32-token block: both parts keep that block's (absolute) scale,
+    so their gradients add up to the merged group's (a group-relative block index would not)."""
+    M, K, N = 128, 16, 12
+    xt, xe, dyt, de = _mx_wgrad_operands(M, K, N, 67)
+    ks = np.arange(K, dtype=np.int64)
+    merged = oracle.mx_gemm_wgrad_rows(xt, xe, dyt, de, np.array([20, 110, 128], np.int32), N,
+                                       np.full(K, 1, np.int32), ks)
+    split = np.array([20, 45, 77, 110, 128], np.int32)
+    parts = [oracle.mx_gemm_wgrad_rows(xt, xe, dyt, de, split, N, np.full(K, g, np.int32), ks)
+             for g in (1, 2, 3)]
+    assert np.allclose(parts[0] + parts[1] + parts[2], merged, rtol=1e-12, atol=0)
+    assert not np.array_equal(parts[0], merged)
