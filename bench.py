@@ -2,11 +2,13 @@
 
 One step = one pass of every hot-path operation over one batch of synthetic input resident in
 HBM:
-  forward   rowwise quant of X, per-expert colwise quant of W (transposed), M-grouped FP8 GEMM;
-            rowwise quant of routed rows gathered in expert order from 2048 token rows (top-8)
-  backward  colwise-grouped transposed quant of X and dY, K-grouped FP8 weight-gradient GEMM;
-            rowwise quant of dY and of W along N, M-grouped FP8 data-gradient GEMM (dX = dY W^T)
+  forward   rowwise quant of X, per-expert colwise quant of W (transposed), M-grouped FP8 GEMM
+  backward  colwise-grouped transposed quant of X and dY, K-grouped FP8 weight-gradient GEMM
   MXFP8     MX rowwise quant of X, MX colwise quant of W, MX grouped GEMM (forward)
+Next rows, timed in passes of their own after the step and reported under "next_rows":
+  rowwise quant of routed rows gathered in expert order from 2048 token rows (top-8);
+  rowwise quant of dY and of W along N, M-grouped FP8 data-gradient GEMM (dX = dY W^T);
+  MX colwise quant of X and dY along tokens, MX K-grouped weight-gradient GEMM.
 Default workload: the DeepSeek-V3-shaped local expert slice (32 experts, hidden 7168,
 intermediate 2048, 16384 routed token rows, Zipf(1.1) group sizes), e4m3fn.
 
@@ -14,8 +16,8 @@ Timing: W untimed warm-up steps, then exactly K timed steps between device synch
 every operation is also bracketed with HIP events on the stream it runs on, giving per-launch
 averages.  The JSON line reports whole-step throughput (algorithmic GEMM flops of the step per
 second of step time, quantization time included), the quantizers' aggregate GB/s, the GEMMs'
-TFLOP/s, a roofline entry for the kernel that takes the most time, and the CPU oracle timed on a
-bounded sample on the host.
+TFLOP/s, a roofline entry for the step kernel that takes the most time, and the CPU oracle timed
+on a bounded sample on the host.
 """
 from __future__ import annotations
 
@@ -37,7 +39,7 @@ FP8_PEAK_TFLOPS = 5000.0    # MI355X dense FP8 (and MXFP8) matrix throughput
 
 WORKLOADS = {
     # name: (workloads-module config, format, ops)
-    "dsv3": ("dsv3_bwd", 1, ("fwd", "gather", "wgrad", "dgrad", "mx")),
+    "dsv3": ("dsv3_bwd", 1, ("fwd", "gather", "wgrad", "dgrad", "mx", "mxwgrad")),
     "dense": ("dense", 1, ("fwd",)),
     "moe16b": ("moe16b", 1, ("fwd",)),
     "tiny": ("tiny", 0, ("fwd", "wgrad")),
@@ -99,7 +101,7 @@ def make_inputs(name, torch, dev):
     w = (torch.randn((E * K, N), generator=gen, device=dev, dtype=torch.float32) * 0.02).to(
         torch.bfloat16)
     dy = None
-    if "wgrad" in ops or "dgrad" in ops:
+    if "wgrad" in ops or "dgrad" in ops or "mxwgrad" in ops:
         dy = torch.randn((M, N), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
     return dict(M=M, K=K, N=N, E=E, fmt=fmt, ops=ops, x=x, w=w, dy=dy,
                 offsets=torch.tensor(offsets, dtype=torch.int32, device=dev),
@@ -142,6 +144,10 @@ class Step:
         if "mx" in d["ops"]:
             self.buf.update(mxq=e(M, K), mxe=e(M, K // 32), mxwt=e(N, E * K),
                             mxwe=e(N, E * K // 32), ymx=e(M, N, dt=bf))
+        if "mxwgrad" in d["ops"]:
+            # MX backward: X and dY quantized along tokens in 32-token blocks (M % 32 == 0)
+            self.buf.update(mxxt=e(K, M), mxxe=e(K, M // 32), mxdyt=e(N, M),
+                            mxdye=e(N, M // 32), mxdw=e(G, K, N, dt=bf))
         self.ldm = ldm
         self.flops = {}
         self.bytes = {}
@@ -158,6 +164,12 @@ class Step:
             self.gemm_bytes["gemm_wgrad"] = K * M + N * M + G * K * N * 2 + G * K * 4 + G * N * 4
             self.bytes["quant_colwise_xT"] = M * K * 3 + G * K * 4
             self.bytes["quant_colwise_dyT"] = M * N * 3 + G * N * 4
+        if "mxwgrad" in d["ops"]:
+            self.flops["gemm_mx_wgrad"] = 2.0 * M * N * K
+            self.gemm_bytes["gemm_mx_wgrad"] = (K * M + N * M + G * K * N * 2 + K * M // 32
+                                                + N * M // 32)
+            self.bytes["mx_quant_colwise_xT"] = M * K * 3 + M * K // 32
+            self.bytes["mx_quant_colwise_dyT"] = M * N * 3 + M * N // 32
         if "gather" in d["ops"]:
             # minimum traffic: each token row read once, every routed row written, index, scales
             self.bytes["quant_rowwise_gather_x"] = (M // 8) * K * 2 + M * K + M * 4 + M * 4
@@ -186,8 +198,11 @@ class Step:
                 fq.GEMM_FWD_MGROUPED, fmt, b["xq"], b["sx"], b["wqt"], b["sw"], d["offsets"],
                 M, N, K, ldb=E * K, b_group_stride=K, c=b["y"])),
         ]
+        # rows beyond the hot-path step (gathered dispatch quant, data gradient, MX backward):
+        # timed in passes of their own after the step
+        extra = []
         if "gather" in d["ops"]:
-            seq += [("quant_rowwise_gather_x", lambda: fq.fp8_quant_rowwise_gather(
+            extra += [("quant_rowwise_gather_x", lambda: fq.fp8_quant_rowwise_gather(
                 d["x"][: M // 8], self.gidx, fmt, q=b["gq"], scales=b["gs"]))]
         if "wgrad" in d["ops"]:
             seq += [
@@ -204,7 +219,7 @@ class Step:
         if "dgrad" in d["ops"]:
             # dX[m, k] = sum_n dY[m, n] W_g[k, n]: the forward mode with W's [K, N] rows of expert
             # g as the per-group B operand (contraction over N)
-            seq += [
+            extra += [
                 ("quant_rowwise_dy", lambda: fq.fp8_quant_rowwise(d["dy"], fmt, q=b["dyq"],
                                                                   scales=b["sdyr"])),
                 ("quant_rowwise_w", lambda: fq.fp8_quant_rowwise(d["w"], fmt, q=b["wqn"],
@@ -224,7 +239,17 @@ class Step:
                     ldb=E * K, b_group_stride=K, ld_sb=E * K // 32, sb_group_stride=K // 32,
                     c=b["ymx"])),
             ]
-        return seq
+        if "mxwgrad" in d["ops"]:
+            extra += [
+                ("mx_quant_colwise_xT", lambda: fq.fp8_mx_quant_colwise(
+                    d["x"], q_t=b["mxxt"], e8m0=b["mxxe"])),
+                ("mx_quant_colwise_dyT", lambda: fq.fp8_mx_quant_colwise(
+                    d["dy"], q_t=b["mxdyt"], e8m0=b["mxdye"])),
+                ("gemm_mx_wgrad", lambda: fq.fp8_mx_grouped_gemm_wgrad(
+                    b["mxxt"], b["mxxe"], b["mxdyt"], b["mxdye"], d["offsets"], M, N, K,
+                    c=b["mxdw"])),
+            ]
+        return seq, extra
 
 
 def cpu_baseline(d, seconds):
@@ -286,6 +311,28 @@ def measured_traffic(kernel):
     return int(rec["traffic_bytes"])
 
 
+def time_passes(torch, seq, warmup, steps):
+    """Average per-op milliseconds over `steps` passes of `seq` after `warmup` passes, each op
+    bracketed by HIP events on the stream it runs on."""
+    if not seq:
+        return {}
+    for _ in range(warmup):
+        for _, fn in seq:
+            fn()
+    torch.cuda.synchronize()
+    evs = {name: [] for name, _ in seq}
+    for _ in range(steps):
+        for name, fn in seq:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            evs[name].append((a, b))
+    torch.cuda.synchronize()
+    return {n: float(np.mean([a.elapsed_time(b) for a, b in v])) for n, v in evs.items()}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -303,7 +350,7 @@ def main():
     torch.cuda.set_device(dev)
     d = make_inputs(args.workload, torch, dev)
     st = Step(fq, torch, d)
-    seq = st.ops()
+    seq, extra = st.ops()
     for _ in range(args.warmup):
         for _, fn in seq:
             fn()
@@ -324,9 +371,9 @@ def main():
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
     per_op = {n: float(np.mean([a.elapsed_time(b) for a, b in v])) for n, v in evs.items()}
+    extra_op = time_passes(torch, extra, args.warmup, args.steps)
 
-    kernels = {}
-    for n, ms in per_op.items():
+    def entry(n, ms):
         ent = {"us": round(ms * 1e3, 2)}
         if n in st.flops:
             tf = st.flops[n] / (ms * 1e-3) / 1e12
@@ -336,11 +383,14 @@ def main():
         if n in st.bytes:
             gb = st.bytes[n] / (ms * 1e-3) / 1e9
             ent.update(GBps=round(gb, 1), frac_hbm_peak=round(gb / HBM_PEAK_GBPS, 4))
-        kernels[n] = ent
-    gemm_ms = sum(per_op[n] for n in st.flops)
-    quant_ms = sum(per_op[n] for n in st.bytes)
-    total_flops = sum(st.flops.values())
-    total_bytes = sum(st.bytes.values())
+        return ent
+
+    kernels = {n: entry(n, ms) for n, ms in per_op.items()}
+    next_rows = {n: entry(n, ms) for n, ms in extra_op.items()}
+    gemm_ms = sum(per_op[n] for n in per_op if n in st.flops)
+    quant_ms = sum(per_op[n] for n in per_op if n in st.bytes)
+    total_flops = sum(st.flops[n] for n in per_op if n in st.flops)
+    total_bytes = sum(st.bytes[n] for n in per_op if n in st.bytes)
     value = total_flops / (ms_step * 1e-3) / 1e12
 
     dom = max(per_op, key=per_op.get)
@@ -366,9 +416,9 @@ def main():
 
     cfg = {"workload": {
         "dsv3": "DeepSeek-V3-shaped local expert slice: 32 experts, hidden 7168, intermediate "
-                "2048, 16384 routed token rows (Zipf 1.1 group sizes); FP8 forward (+ rowwise "
-                "quant gathered in expert order from 2048 tokens x top-8) + weight-gradient + "
-                "data-gradient + MXFP8 forward",
+                "2048, 16384 routed token rows (Zipf 1.1 group sizes); step: FP8 forward + "
+                "weight-gradient + MXFP8 forward; next_rows: rowwise quant gathered in expert "
+                "order from 2048 tokens x top-8, data gradient, MXFP8 weight gradient",
         "dense": "Llama3-8B-style FFN GEMM: M=8192, K=4096, N=14336, G=1; FP8 forward",
         "moe16b": "DeepSeek-MoE-16B-shaped experts: 64 experts, K=2048, N=1408, 49152 routed "
                   "rows (top-6, Zipf 1.1); FP8 forward",
@@ -389,6 +439,7 @@ def main():
         "gemm_TFLOPs": round(total_flops / (gemm_ms * 1e-3) / 1e12, 1),
         "gemm_frac_mfma_peak": round(total_flops / (gemm_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
         "kernels": kernels,
+        "next_rows": next_rows,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -42,6 +42,8 @@ SIGNATURES = {
     "fp8_mx_quant_colwise": (_I, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P]),
     "fp8_mx_grouped_gemm": (_I, [_P, _I64, _P, _I64, _P, _I64, _I64, _P, _I64, _I64, _P, _I32,
                                  _I64, _I64, _I64, _P, _I64, _P]),
+    "fp8_mx_grouped_gemm_wgrad": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I32, _I64,
+                                       _I64, _I64, _P, _I64, _P]),
 }
 
 
@@ -217,4 +219,21 @@ def fp8_mx_grouped_gemm(a: torch.Tensor, a_e8m0: torch.Tensor, b: torch.Tensor,
                                    _ptr(offsets), groups, M, N, K, _ptr(c), c.stride(0),
                                    _stream(a))
     _check("fp8_mx_grouped_gemm", st)
+    return c
+
+
+def fp8_mx_grouped_gemm_wgrad(a: torch.Tensor, a_e8m0: torch.Tensor, b: torch.Tensor,
+                              b_e8m0: torch.Tensor, offsets: torch.Tensor, M: int, N: int,
+                              K: int, c: torch.Tensor | None = None):
+    """MX weight gradient: a = XqT [K, lda >= M], b = dYqT [N, ldb >= M] with E8M0 per 32
+    tokens (fp8_mx_quant_colwise outputs).  Returns bf16 [G, K, N]."""
+    _dev(a, "a")
+    groups = offsets.numel()
+    if c is None:
+        c = torch.empty((groups, K, N), dtype=torch.bfloat16, device=a.device)
+    st = lib().fp8_mx_grouped_gemm_wgrad(_ptr(a), a.stride(0), _ptr(a_e8m0), a_e8m0.stride(0),
+                                         _ptr(b), b.stride(0), _ptr(b_e8m0), b_e8m0.stride(0),
+                                         _ptr(offsets), groups, M, N, K, _ptr(c), c.stride(-2),
+                                         _stream(a))
+    _check("fp8_mx_grouped_gemm_wgrad", st)
     return c

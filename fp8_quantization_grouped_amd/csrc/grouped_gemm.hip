@@ -222,6 +222,9 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
     const int wm = wave >> 1, wn = wave & 1;
     constexpr bool FNUZ = FMT == FP8Q_E4M3FNUZ;
     const int64_t tiles_per_group = (int64_t)p.nt_k * p.nt_n;
+    // weight gradient: a tile's contraction starts at its group's first token rounded down to
+    // 16 (one LDS chunk), or to 32 for MX so that the steps' 32-token blocks are the scale blocks
+    constexpr int64_t KALIGN = MX ? 31 : 15;
 
     if (OFF_LDS) {
         for (int i = t; i < p.G; i += 256) s_off[i] = p.offsets[i];
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
             if (i < p.G) {
                 int64_t lo, hi;
                 rows_of(i, lo, hi);
-                const int64_t ks = lo & ~(int64_t)15;
+                const int64_t ks = lo & ~KALIGN;
                 const int64_t nk = hi > ks ? (hi - ks + GK - 1) / GK : 0;
                 k = ((long long)nk << 11) | (long long)(GMAX - 1 - i);
             }
@@ -384,7 +387,7 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
             T.row_hi = T.row_lo + GT < p.K ? T.row_lo + GT : (int)p.K;
             T.kb_lo = (int)glo;
             T.kb_hi = (int)ghi;
-            T.kstart = (int)(glo & ~(int64_t)15);
+            T.kstart = (int)(glo & ~KALIGN);
             T.a_rows = T.row_hi - T.row_lo;
         }
         T.nk = T.kb_hi > T.kstart ? (T.kb_hi - T.kstart + GK - 1) / GK : 0;
@@ -466,7 +469,7 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
             sa_pack = sb_pack = 0;
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-                const bool ok = kpos + 32 * j < p.K;
+                const bool ok = kpos + 32 * j < (MODE == MODE_FWD ? p.K : p.M);
                 const uint32_t oa = (ok && t < T.a_rows) ? (uint32_t)(t * p.ld_sa + kb0 + j) : OOB;
                 const uint32_t ob = (ok && t < T.b_rows) ? (uint32_t)(t * p.ld_sb + kb0 + j) : OOB;
                 const uint32_t ea =
@@ -502,7 +505,11 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
 #pragma unroll
         for (int i = 0; i < 8; i++) part(P, i);
     };
-    // MX scales are staged in registers and written to LDS after the step's matrix work.
+    // MX_BYTES: a step's scale bytes are loaded into registers with its operand loads and
+    // written to LDS at the top of that step, after its wait for the loads.  Using them any
+    // earlier would wait for every operand load issued after them as well (the vector-memory
+    // counter completes in issue order), serializing the prefetch.
+    bool scales_pending = false;
     auto commit_scales = [&](int stage) {
         if (MXV == MX_BYTES) {
             sscale[stage][0][t] = sa_pack;
@@ -515,7 +522,7 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
     int stage0 = 0;  // LDS stage holding the current tile's first step
     if (have && cur.nk > 0) {
         issue(cur, cur.kstart, 0);
-        commit_scales(0);
+        scales_pending = true;
     }
     const int kg = lane >> 4, lr = lane & 15, lq = lane >> 4;
     while (have) {
@@ -530,6 +537,10 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
             const int cur_st = (stage0 + (kk & 1)) & 1;
             const int kpos = cur.kstart + kk * GK;
             wait_vm0();  // this wave's loads of step kk have landed
+            if (MXV == MX_BYTES && scales_pending) {
+                commit_scales(cur_st);  // read after this step's barrier
+                scales_pending = false;
+            }
             if (MODE == MODE_WGRAD && (kpos < cur.kb_lo || kpos + GK > cur.kb_hi)) {
                 // zero the activation bytes of neighbouring groups in the straddling chunks
                 __syncthreads();
@@ -608,7 +619,7 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
                             bf[j], af, acc[i][j], 0, 0, 0, 0, 0, 0);
                 }
             }
-            if (kk + 1 < cur.nk || next_issued) commit_scales(cur_st ^ 1);
+            if (kk + 1 < cur.nk || next_issued) scales_pending = true;
         }
         if (cur.nk == 0) {
             // nothing was computed; start the next tile's first step in the free stage once
@@ -618,7 +629,7 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(const GemmArgs p) {
             have_next = next_tile(nxt);
             if (have_next && nxt.nk > 0) {
                 issue(nxt, nxt.kstart, stage0);
-                commit_scales(stage0);
+                scales_pending = true;
             }
         }
 
@@ -745,6 +756,31 @@ extern "C" fp8q_status_t fp8_grouped_gemm(fp8q_gemm_mode_t mode, fp8q_format_t f
         return launch_gemm<FP8Q_E4M3FNUZ, MODE_WGRAD, MX_NONE>(p, stream);
     }
     return FP8Q_ERR_INVALID_ARG;
+}
+
+extern "C" fp8q_status_t fp8_mx_grouped_gemm_wgrad(const uint8_t* a, int64_t lda,
+                                                   const uint8_t* a_e8m0, int64_t ld_sa,
+                                                   const uint8_t* b, int64_t ldb,
+                                                   const uint8_t* b_e8m0, int64_t ld_sb,
+                                                   const int32_t* offsets, int32_t groups,
+                                                   int64_t M, int64_t N, int64_t K, uint16_t* c,
+                                                   int64_t ldc, hipStream_t stream) {
+    using namespace fp8q;
+    if (groups < 1 || M < 0 || N < 0 || K < 0 || ldc < N || !offsets || lda < M || ldb < M ||
+        ld_sa < M / 32 || ld_sb < M / 32)
+        return FP8Q_ERR_INVALID_ARG;
+    if (M % 32) return FP8Q_ERR_INVALID_ARG;
+    if (K == 0 || N == 0) return FP8Q_OK;
+    if (!a_e8m0 || !b_e8m0 || !c || (M > 0 && (!a || !b))) return FP8Q_ERR_INVALID_ARG;
+    if (lda % 16 || ldb % 16 || !fp8q_aligned(a, 16) || !fp8q_aligned(b, 16) ||
+        !offsets_fit(lda, ldb) || !offsets_fit(ld_sa, ld_sb))
+        return FP8Q_ERR_UNSUPPORTED;
+    GemmArgs p{};
+    p.a = a; p.lda = lda; p.a_e8 = a_e8m0; p.ld_sa = ld_sa; p.b = b; p.ldb = ldb;
+    p.bgs = 0; p.b_e8 = b_e8m0; p.ld_sb = ld_sb; p.sbgs = 0;
+    p.offsets = offsets; p.G = groups; p.M = M; p.N = N; p.K = K; p.c = c; p.ldc = ldc;
+    // per-step byte loads of the scales: a tile's first 32-token block need not be 16-aligned
+    return launch_gemm<FP8Q_E4M3FN, MODE_WGRAD, MX_BYTES>(p, stream);
 }
 
 extern "C" fp8q_status_t fp8_mx_grouped_gemm(const uint8_t* a, int64_t lda, const uint8_t* a_e8m0,

@@ -199,6 +199,28 @@ fp8q_status_t fp8_mx_grouped_gemm(const uint8_t* a, int64_t lda, const uint8_t* 
                                   int32_t groups, int64_t M, int64_t N, int64_t K, uint16_t* c,
                                   int64_t ldc, hipStream_t stream);
 
+/* MXFP8 grouped GEMM, weight gradient (groups along the token dimension, which is the
+ * contraction) -- the MX backward (fosswire.org "AMD Primus adds FP8/MXFP8 kernels ...",
+ * section "What Primus adds for MoE training on MI355X": MXFP8 grouped GEMMs for the expert
+ * FFNs; block rule of OCP MX v1.0).  The operands are the transposed MX quantizations of X
+ * [M, K] and dY [M, N] from fp8_mx_quant_colwise: scale blocks are 32 consecutive tokens counted
+ * from token 0, so a block may straddle a group boundary; it keeps its one scale and each group
+ * sums only its own tokens:
+ *   c[(g*K + k)*ldc + n] = bf16( sum_{m in g} dec(a[k,m]) 2^(ea[k, m/32]) dec(b[n,m]) 2^(eb[n, m/32]) )
+ * with ea = a_e8m0[k*ld_sa + m/32] - 127, eb = b_e8m0[n*ld_sb + m/32] - 127; empty groups write
+ * zeros.
+ *   a       XqT u8 [K][lda], lda >= M;  a_e8m0 [K][ld_sa], ld_sa >= M/32
+ *   b       dYqT u8 [N][ldb], ldb >= M; b_e8m0 [N][ld_sb], ld_sb >= M/32
+ *   offsets int32 [groups] device (as for the FP8 weight gradient); M % 32 == 0
+ *   c       bf16 [groups][K][ldc], ldc >= N
+ * Limits as for the FP8 weight-gradient GEMM, plus 256 * ld_sa, 256 * ld_sb < 2^31. */
+fp8q_status_t fp8_mx_grouped_gemm_wgrad(const uint8_t* a, int64_t lda, const uint8_t* a_e8m0,
+                                        int64_t ld_sa, const uint8_t* b, int64_t ldb,
+                                        const uint8_t* b_e8m0, int64_t ld_sb,
+                                        const int32_t* offsets, int32_t groups, int64_t M,
+                                        int64_t N, int64_t K, uint16_t* c, int64_t ldc,
+                                        hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

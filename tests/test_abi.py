@@ -29,6 +29,7 @@ def test_header_declares_the_hot_path():
     for must in ("fp8_quant_rowwise", "fp8_quant_rowwise_gather", "fp8_quant_colwise_grouped",
                  "fp8_grouped_gemm",
                  "fp8_mx_quant_rowwise", "fp8_mx_quant_colwise", "fp8_mx_grouped_gemm",
+                 "fp8_mx_grouped_gemm_wgrad",
                  "fp8_quant_colwise_grouped_workspace_size", "fp8q_status_string",
                  "fp8q_abi_version"):
         assert must in names
@@ -93,6 +94,15 @@ def test_argument_errors_are_caught_on_the_host(lib):
     assert g(0, 1, dummy, 16, dummy, dummy, 16, 0, dummy, dummy, 0, 4, 4, 16, dummy, 4, None) == 1
     assert g(1, 1, dummy, 16, dummy, dummy, 16, 16, dummy, dummy, 1, 4, 4, 16, dummy, 4,
              None) == 1  # wgrad needs b_group_stride == 0
+    mw = lib.fp8_mx_grouped_gemm_wgrad
+    mw.restype = I
+    mw.argtypes = [P, I64, P, I64, P, I64, P, I64, P, ctypes.c_int32, I64, I64, I64, P, I64, P]
+    assert mw(dummy, 48, dummy, 2, dummy, 48, dummy, 2, dummy, 1, 48, 16, 16, dummy, 16,
+              None) == 1  # M not a multiple of 32
+    assert mw(dummy, 64, dummy, 1, dummy, 64, dummy, 2, dummy, 1, 64, 16, 16, dummy, 16,
+              None) == 1  # scale rows shorter than M/32
+    assert mw(dummy, 64, dummy, 2, dummy, 64, dummy, 2, dummy, 1, 64, 0, 16, dummy, 16,
+              None) == 0  # N == 0: no-op
 
 
 def test_device_code_has_no_generic_memory_instructions():

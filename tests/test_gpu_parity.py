@@ -15,6 +15,7 @@ import torch
 
 import oracle
 import workloads
+from tests.mfma_bound import check_tol_hw, mx_wgrad_block_truncation_bound
 from tests import pinlib
 
 pytestmark = pytest.mark.gpu
@@ -434,6 +435,39 @@ def test_mx_gemm_padded_scale_rows(fq):
     ref = oracle.mx_gemm_fwd_rows(qa, ea_p, qbt, E * K, K, eb_p.reshape(-1), ld, N * ld, off, N,
                                   K, np.arange(M))
     gemm_tol_check(c.float().cpu().numpy(), ref, "mx padded scale rows")
+
+
+# (M tokens, K, N, offsets): groups that start and end inside 32-token scale blocks, empty
+# groups, ragged K and N tiles, one long group.
+MX_WGRAD_CASES = [
+    (256, 160, 96, [40, 40, 150, 256]),
+    (512, 256, 128, [512]),
+    (1024, 300, 72, [0, 17, 300, 301, 640, 1000, 1024]),
+    (2048, 128, 256, [700, 2048]),
+]
+
+
+@pytest.mark.parametrize("case", MX_WGRAD_CASES)
+def test_mx_gemm_wgrad_parity(fq, case):
+    """MX weight gradient from the transposed MX quantizations of X and dY (32-token blocks
+    counted from token 0): every dW element against the oracle."""
+    M, K, N, off = case
+    off = np.asarray(off, np.int32)
+    G = off.size
+    x = workloads.make_matrix(950 + M, M, K, 1.0, 0.0)
+    dy = workloads.make_matrix(951 + M, M, N)
+    xt, xe = oracle.mx_quant_colwise(x)      # [K, M], [K, M/32]
+    dyt, de = oracle.mx_quant_colwise(dy)    # [N, M], [N, M/32]
+    c = fq.fp8_mx_grouped_gemm_wgrad(torch.from_numpy(xt).to(DEV), torch.from_numpy(xe).to(DEV),
+                                     torch.from_numpy(dyt).to(DEV), torch.from_numpy(de).to(DEV),
+                                     dev_i32(off), M, N, K)
+    gi = np.repeat(np.arange(G, dtype=np.int32), K)
+    ki = np.tile(np.arange(K, dtype=np.int64), G)
+    ref = oracle.mx_gemm_wgrad_rows(xt, xe, dyt, de, off, N, gi, ki)
+    # a group of ~1300 tokens gives |dW| ~ 40, so an element cancelling to ~1e-3 can miss the
+    # 1e-3 absolute bar by the matrix cores' block truncation: allowed (rarely) up to that bound
+    hw = mx_wgrad_block_truncation_bound(xt, xe, dyt, de, off, gi, ki)
+    check_tol_hw(c.float().cpu().numpy().reshape(G * K, N), ref, hw, f"mx wgrad {case}")
 
 
 # ----------------------------------------------------------------------------- argument errors
