@@ -43,6 +43,19 @@ __device__ __forceinline__ uint4 ld_nt16(const void* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// 8- and 16-byte stores with the non-temporal hint (output written once and not read back by
+// the same kernel).
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void st_nt8(void* p, uint32_t a, uint32_t b) {
+    __builtin_nontemporal_store(u32x2_t{a, b}, reinterpret_cast<u32x2_t*>(p));
+}
+__device__ __forceinline__ void st_nt16(void* p, uint4 v) {
+    __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
+}
+// Outputs larger than this go out with streaming stores: they cannot stay in the 256 MB
+// last-level cache for their consumer anyway (measured on the quantizers' outputs).
+constexpr double kStreamBytes = 128.0 * 1024 * 1024;
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

@@ -17,12 +17,14 @@
 //      it is in (packed 16-bit max on bf16 magnitude bits), and when the group changes reduces
 //      them to 64 column maxima (lane shuffles, then LDS across the 4 waves) and publishes them
 //      with relaxed device-scope atomicMax on the bf16 magnitude bits (exact: for finite values
-//      their integer order is the value order).
-//   2. colwise_cast_kernel: walks the same tiles, turns the finished maxima into scales (per
-//      group in LDS, reused while the groups do not change), scales/clamps/converts along rows
-//      so each lane holds 8 consecutive output bytes of each of its 8 columns, transposes
-//      through LDS and writes 16-byte chunks of the column-major output (16 lanes cover one
-//      column's 256 contiguous bytes).
+//      their integer order is the value order).  An input too large to stay in the 256 MB
+//      last-level cache until the second pass is read with streaming loads.
+//   2. colwise_cast_kernel: one 256x64 tile per block (more resident blocks hide the load
+//      latency better than a register prefetch of the next tile), streaming loads (last read);
+//      turns the finished maxima into scales (per group in LDS), scales/clamps/converts along
+//      rows one column at a time so each lane produces 8 consecutive output bytes of each of its
+//      8 columns, transposes through LDS and writes 16-byte chunks of the column-major output
+//      with streaming stores (16 lanes cover one column's 256 contiguous bytes).
 // The group offsets are staged in LDS once per block, so finding a row's group is a short
 // search in LDS instead of a chain of dependent global loads.  The block whose tile contains
 // a group's first row writes that group's scales; the last row tile also writes groups that
@@ -35,7 +37,8 @@ constexpr int CW_TR = 256;              // tile rows
 constexpr int CW_TC = 64;               // tile columns
 constexpr int CW_STR = CW_TR + 16;      // LDS bytes per transposed column (16-byte aligned)
 constexpr int CW_GB = 8;                // groups per scale batch in LDS
-constexpr int CW_TPB = 4;               // row tiles per block
+constexpr int CW_TPB = 4;               // row tiles per block (maxima pass)
+constexpr int CW_TPB_CAST = 1;          // row tiles per block (cast pass)
 constexpr int CW_GLDS = 2048;           // groups whose offsets are staged in LDS
 
 // Group offsets as the kernels read them: from an LDS copy staged once per block (LDS, the
@@ -85,7 +88,7 @@ __device__ __forceinline__ Offs<LDS> stage_offsets(const int32_t* __restrict__ o
 
 // The lane's 8x8 block: rows r0 + 8*qd + i (i < 8), columns c0 + 8*o .. +7, as bf16 bits
 // packed two per dword (column 2d in the low half of dword d).  Out-of-range elements are 0.
-template <bool VEC>
+template <bool VEC, bool NT = false>
 __device__ __forceinline__ void cw_load(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                         int64_t ld_x, int64_t r0, int64_t c0, int o, int qd,
                                         uint4 v[8]) {
@@ -94,7 +97,8 @@ __device__ __forceinline__ void cw_load(const uint16_t* __restrict__ x, int64_t 
     for (int i = 0; i < 8; i++) {
         const int64_t r = r0 + 8 * qd + i;
         if (VEC) {
-            v[i] = (r < R && c < C) ? *reinterpret_cast<const uint4*>(x + r * ld_x + c)
+            v[i] = (r < R && c < C) ? (NT ? ld_nt16(x + r * ld_x + c)
+                                          : *reinterpret_cast<const uint4*>(x + r * ld_x + c))
                                     : make_uint4(0, 0, 0, 0);
         } else {
             uint32_t e[8];
@@ -106,12 +110,18 @@ __device__ __forceinline__ void cw_load(const uint16_t* __restrict__ x, int64_t 
     }
 }
 
+// Column j (0..7) of a lane's 8-column row chunk as fp32 (column 2d in the low half of dword d).
+__device__ __forceinline__ float cw_elem(const uint4& r, int j) {
+    const uint32_t w = j < 2 ? r.x : j < 4 ? r.y : j < 6 ? r.z : r.w;
+    return (j & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
 __global__ void cw_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
         p[i] = 0u;
 }
 
-template <bool VEC, bool LDS>
+template <bool VEC, bool LDS, bool NT>
 __global__ __launch_bounds__(256) void colwise_amax_kernel(const uint16_t* __restrict__ x,
                                                            int64_t R, int64_t C, int64_t ld_x,
                                                            const int32_t* __restrict__ offsets,
@@ -152,11 +162,11 @@ __global__ __launch_bounds__(256) void colwise_amax_kernel(const uint16_t* __res
         m0 = m1 = m2 = m3 = 0;
     };
     uint4 v[8], vn[8];
-    cw_load<VEC>(x, R, C, ld_x, rb, c0, o, qd, v);
+    cw_load<VEC, NT>(x, R, C, ld_x, rb, c0, o, qd, v);
     for (int k = 0; k < CW_TPB; k++) {
         const int64_t r0 = rb + (int64_t)k * CW_TR;
         if (r0 >= R) break;  // block-uniform
-        if (k + 1 < CW_TPB) cw_load<VEC>(x, R, C, ld_x, r0 + CW_TR, c0, o, qd, vn);
+        if (k + 1 < CW_TPB) cw_load<VEC, NT>(x, R, C, ld_x, r0 + CW_TR, c0, o, qd, vn);
         const int64_t r_end = r0 + CW_TR < R ? r0 + CW_TR : R;
         const int g_first = off.group_of(r0);
         const int g_last = off.group_of(r_end - 1);
@@ -193,7 +203,7 @@ __global__ __launch_bounds__(256) void colwise_cast_kernel(
     const int32_t* __restrict__ offsets, int G, const uint32_t* __restrict__ amax,
     uint8_t* __restrict__ qt, int64_t ld_qt, float* __restrict__ scales) {
     const int t = threadIdx.x, o = t & 7, qd = t >> 3;
-    const int64_t rb = (int64_t)blockIdx.x * CW_TR * CW_TPB, c0 = (int64_t)blockIdx.y * CW_TC;
+    const int64_t rb = (int64_t)blockIdx.x * CW_TR * CW_TPB_CAST, c0 = (int64_t)blockIdx.y * CW_TC;
     __shared__ __align__(16) float sc[CW_GB][CW_TC];
     __shared__ __align__(16) uint8_t tile[CW_TC * CW_STR];
     const Offs<LDS> off = stage_offsets<LDS>(offsets, G);
@@ -201,7 +211,7 @@ __global__ __launch_bounds__(256) void colwise_cast_kernel(
     // Scales of the groups this block owns (first row inside one of its tiles; the block with
     // the last tile also owns groups starting at or after the end, i.e. trailing empty groups).
     {
-        const int64_t r_stop = rb + (int64_t)CW_TR * CW_TPB;
+        const int64_t r_stop = rb + (int64_t)CW_TR * CW_TPB_CAST;
         const bool last_block = r_stop >= R;
         for (int g = off.first_starting_at(rb); g < G; g++) {
             if (!last_block && off.start(g) >= r_stop) break;
@@ -215,11 +225,11 @@ __global__ __launch_bounds__(256) void colwise_cast_kernel(
 
     int sc_lo = -1, sc_hi = -2;  // groups held in sc (block-uniform)
     uint4 v[8], vn[8];
-    cw_load<VEC>(x, R, C, ld_x, rb, c0, o, qd, v);
-    for (int k = 0; k < CW_TPB; k++) {
+    cw_load<VEC, true>(x, R, C, ld_x, rb, c0, o, qd, v);
+    for (int k = 0; k < CW_TPB_CAST; k++) {
         const int64_t r0 = rb + (int64_t)k * CW_TR;
         if (r0 >= R) break;  // block-uniform
-        if (k + 1 < CW_TPB) cw_load<VEC>(x, R, C, ld_x, r0 + CW_TR, c0, o, qd, vn);
+        if (k + 1 < CW_TPB_CAST) cw_load<VEC, true>(x, R, C, ld_x, r0 + CW_TR, c0, o, qd, vn);
         const int64_t r_end = r0 + CW_TR < R ? r0 + CW_TR : R;
         const int g_first = off.group_of(r0);
         const int g_last = off.group_of(r_end - 1);
@@ -234,11 +244,9 @@ __global__ __launch_bounds__(256) void colwise_cast_kernel(
                 gid[i] = r < r_end ? g : -1;
             }
         }
-        float y[8][8];
+        uint32_t ow0[8], ow1[8];
 #pragma unroll
-        for (int i = 0; i < 8; i++)
-#pragma unroll
-            for (int j = 0; j < 8; j++) y[i][j] = 0.0f;
+        for (int j = 0; j < 8; j++) ow0[j] = ow1[j] = 0u;
         for (int gb = g_first; gb <= g_last; gb += CW_GB) {
             const int gb_hi = gb + CW_GB - 1 < g_last ? gb + CW_GB - 1 : g_last;
             if (!(gb >= sc_lo && gb_hi <= sc_hi)) {
@@ -256,31 +264,46 @@ __global__ __launch_bounds__(256) void colwise_cast_kernel(
                 sc_lo = gb;
                 sc_hi = gb + CW_GB - 1;
             }
+            if (g_first == g_last) {
+                const int kk = g_first - sc_lo;
+                const float4 sa = *reinterpret_cast<const float4*>(&sc[kk][8 * o]);
+                const float4 sb = *reinterpret_cast<const float4*>(&sc[kk][8 * o + 4]);
+                const float sj[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const int kk = gid[i] - sc_lo;
-                if (gid[i] >= gb && gid[i] <= gb_hi) {
-                    const float4 sa = *reinterpret_cast<const float4*>(&sc[kk][8 * o]);
-                    const float4 sb = *reinterpret_cast<const float4*>(&sc[kk][8 * o + 4]);
-                    y[i][0] = bf16_lo(v[i].x) * sa.x;
-                    y[i][1] = bf16_hi(v[i].x) * sa.y;
-                    y[i][2] = bf16_lo(v[i].y) * sa.z;
-                    y[i][3] = bf16_hi(v[i].y) * sa.w;
-                    y[i][4] = bf16_lo(v[i].z) * sb.x;
-                    y[i][5] = bf16_hi(v[i].z) * sb.y;
-                    y[i][6] = bf16_lo(v[i].w) * sb.z;
-                    y[i][7] = bf16_hi(v[i].w) * sb.w;
+                for (int j = 0; j < 8; j++) {
+                    float y[8];
+#pragma unroll
+                    for (int i = 0; i < 8; i++) y[i] = cw_elem(v[i], j) * sj[j];
+                    ow0[j] = enc4<FMT>(y[0], y[1], y[2], y[3]);
+                    ow1[j] = enc4<FMT>(y[4], y[5], y[6], y[7]);
+                }
+            } else {
+#pragma unroll
+                for (int pr = 0; pr < 4; pr++) {
+                    float y[2][8];
+#pragma unroll
+                    for (int ii = 0; ii < 2; ii++) {
+                        const int i = 2 * pr + ii;
+                        const bool in = gid[i] >= gb && gid[i] <= gb_hi;
+                        const int kk = in ? gid[i] - sc_lo : 0;
+                        const float4 sa = *reinterpret_cast<const float4*>(&sc[kk][8 * o]);
+                        const float4 sb = *reinterpret_cast<const float4*>(&sc[kk][8 * o + 4]);
+                        const float sj[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+#pragma unroll
+                        for (int j = 0; j < 8; j++) y[ii][j] = in ? cw_elem(v[i], j) * sj[j] : 0.0f;
+                    }
+#pragma unroll
+                    for (int j = 0; j < 8; j++) {
+                        const uint32_t w = enc4<FMT>(y[0][j], y[1][j], 0.0f, 0.0f) << (16 * (pr & 1));
+                        if (pr < 2) ow0[j] |= w; else ow1[j] |= w;
+                    }
                 }
             }
         }
         __syncthreads();  // previous tile's transposed bytes have been stored
-        // Encode along rows: column j of the lane gets the bytes of rows 8*qd .. 8*qd+7.
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const uint32_t w0 = enc4<FMT>(y[0][j], y[1][j], y[2][j], y[3][j]);
-            const uint32_t w1 = enc4<FMT>(y[4][j], y[5][j], y[6][j], y[7][j]);
-            *reinterpret_cast<uint2*>(&tile[(8 * o + j) * CW_STR + 8 * qd]) = make_uint2(w0, w1);
-        }
+        for (int j = 0; j < 8; j++)
+            *reinterpret_cast<uint2*>(&tile[(8 * o + j) * CW_STR + 8 * qd]) = make_uint2(ow0[j], ow1[j]);
         __syncthreads();
 #pragma unroll
         for (int kq = 0; kq < 4; kq++) {
@@ -291,14 +314,15 @@ __global__ __launch_bounds__(256) void colwise_cast_kernel(
             const uint8_t* src = &tile[col * CW_STR + 16 * seg];
             uint8_t* dst = qt + c * ld_qt + r;
             if (VEC_OUT && r + 16 <= R) {
-                *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+                st_nt16(dst, *reinterpret_cast<const uint4*>(src));  // measured faster at every size
             } else {
                 for (int bb = 0; bb < 16; bb++)
                     if (r + bb < R) dst[bb] = src[bb];
             }
         }
 #pragma unroll
-        for (int i = 0; i < 8; i++) v[i] = vn[i];
+        for (int i = 0; i < 8; i++)
+            if (k + 1 < CW_TPB_CAST) v[i] = vn[i];
     }
 }
 
@@ -306,7 +330,7 @@ template <int FMT, bool VEC, bool VEC_OUT>
 static void launch_cast(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x,
                         const int32_t* offsets, int G, const uint32_t* ws, uint8_t* qt,
                         int64_t ld_qt, float* s, hipStream_t stream) {
-    const int64_t rt = R > 0 ? (R + CW_TR * CW_TPB - 1) / (CW_TR * CW_TPB) : 1;
+    const int64_t rt = R > 0 ? (R + CW_TR * CW_TPB_CAST - 1) / (CW_TR * CW_TPB_CAST) : 1;
     const int64_t ct = (C + CW_TC - 1) / CW_TC;
     const dim3 grid((unsigned)rt, (unsigned)ct);
     if (G <= CW_GLDS)
@@ -331,14 +355,22 @@ static fp8q_status_t colwise_run(const uint16_t* x, int64_t R, int64_t C, int64_
         const dim3 grid((unsigned)((R + CW_TR * CW_TPB - 1) / (CW_TR * CW_TPB)),
                         (unsigned)((C + CW_TC - 1) / CW_TC));
         const bool lds = G <= CW_GLDS;
-        if (vec && lds)
-            colwise_amax_kernel<true, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws);
+        // The cast pass reads the input again.  An input of up to 128 MB can stay in the 256 MB
+        // last-level cache until then, so this pass reads it with ordinary loads; a larger one
+        // cannot, and is read with streaming loads.
+        const bool nt = (double)R * (double)ld_x * 2.0 > kStreamBytes;
+        if (vec && lds && nt)
+            colwise_amax_kernel<true, true, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws);
+        else if (vec && lds)
+            colwise_amax_kernel<true, true, false><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws);
+        else if (vec && nt)
+            colwise_amax_kernel<true, false, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws);
         else if (vec)
-            colwise_amax_kernel<true, false><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws);
+            colwise_amax_kernel<true, false, false><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws);
         else if (lds)
-            colwise_amax_kernel<false, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws);
+            colwise_amax_kernel<false, true, false><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws);
         else
-            colwise_amax_kernel<false, false><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws);
+            colwise_amax_kernel<false, false, false><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws);
     }
     if (vec && vec_out) launch_cast<FMT, true, true>(x, R, C, ld_x, offsets, G, ws, qt, ld_qt, s, stream);
     else if (vec) launch_cast<FMT, true, false>(x, R, C, ld_x, offsets, G, ws, qt, ld_qt, s, stream);

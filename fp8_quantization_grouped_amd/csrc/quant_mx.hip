@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void mx_rowwise_kernel(const uint16_t* __restr
                                                   bf16_lo(v[j].y) * inv, bf16_hi(v[j].y) * inv);
             const uint32_t w1 = enc4<FP8Q_E4M3FN>(bf16_lo(v[j].z) * inv, bf16_hi(v[j].z) * inv,
                                                   bf16_lo(v[j].w) * inv, bf16_hi(v[j].w) * inv);
-            *reinterpret_cast<uint2*>(q + row * ld_q + ch * 8) = make_uint2(w0, w1);
+            st_nt8(q + row * ld_q + ch * 8, w0, w1);  // streaming: measured faster
             if ((threadIdx.x & 3) == 0) e8[row * ld_s + (ch >> 2)] = (uint8_t)eb;
         }
     }
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void mx_colwise_kernel(const uint16_t* __restr
                                                          int64_t R, int64_t C, int64_t ld_x,
                                                          uint8_t* __restrict__ qt, int64_t ld_qt,
                                                          uint8_t* __restrict__ e8, int64_t ld_s,
-                                                         bool vec_out) {
+                                                         bool vec_out, bool nt_out) {
     const int t = threadIdx.x, o = t & 7, qd = t >> 3;
     const int64_t r0 = (int64_t)blockIdx.x * MXC_TR, c0 = (int64_t)blockIdx.y * MXC_TC;
     __shared__ __align__(16) uint8_t tile[MXC_TC * MXC_STR];
@@ -131,7 +131,8 @@ __global__ __launch_bounds__(256) void mx_colwise_kernel(const uint16_t* __restr
         const uint8_t* src = &tile[col * MXC_STR + 16 * seg];
         uint8_t* dst = qt + cc * ld_qt + r;
         if (vec_out && r + 16 <= R) {
-            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+            if (nt_out) st_nt16(dst, *reinterpret_cast<const uint4*>(src));  // block-uniform
+            else *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
         } else {
             for (int bb = 0; bb < 16; bb++)
                 if (r + bb < R) dst[bb] = src[bb];
@@ -175,7 +176,8 @@ extern "C" fp8q_status_t fp8_mx_quant_colwise(const uint16_t* x, int64_t rows, i
     if (rt > 0x7FFFFFFFLL || ct > 65535) return FP8Q_ERR_UNSUPPORTED;
     const bool vec_out = (ld_qt % 16 == 0) && fp8q_aligned(q_t, 16);
     fp8q::mx_colwise_kernel<<<dim3((unsigned)rt, (unsigned)ct), dim3(256), 0, stream>>>(
-        x, rows, cols, ld_x, q_t, ld_qt, e8m0, ld_s, vec_out);
+        x, rows, cols, ld_x, q_t, ld_qt, e8m0, ld_s, vec_out,
+        (double)cols * (double)ld_qt > fp8q::kStreamBytes);
     FP8Q_CHECK_LAUNCH();
     return FP8Q_OK;
 }

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void rowwise_vec_kernel(const uint16_t* __rest
                                                           int64_t ld_q,
                                                           float* __restrict__ scales,
                                                           const int32_t* __restrict__ index,
-                                                          int64_t src_rows) {
+                                                          int64_t src_rows, bool nt_out) {
     constexpr int RPB = 4 / WPR;   // rows per 256-thread block
     constexpr int TPR = 64 * WPR;  // threads per row
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -81,7 +81,8 @@ __global__ __launch_bounds__(256) void rowwise_vec_kernel(const uint16_t* __rest
                                     bf16_lo(v[j].y) * sm, bf16_hi(v[j].y) * sm);
             uint32_t w1 = enc4<FMT>(bf16_lo(v[j].z) * sm, bf16_hi(v[j].z) * sm,
                                     bf16_lo(v[j].w) * sm, bf16_hi(v[j].w) * sm);
-            qr[c] = make_uint2(w0, w1);
+            if (nt_out) st_nt8(qr + c, w0, w1);  // block-uniform branch
+            else qr[c] = make_uint2(w0, w1);
         }
     }
 }
@@ -126,8 +127,9 @@ static void launch_vec(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
                        hipStream_t stream) {
     constexpr int RPB = 4 / WPR;
     const int64_t blocks = (rows + RPB - 1) / RPB;
+    const bool nt_out = (double)rows * (double)ld_q > kStreamBytes;
     rowwise_vec_kernel<FMT, WPR, NV><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
-        x, rows, cols, ld_x, q, ld_q, s, index, src_rows);
+        x, rows, cols, ld_x, q, ld_q, s, index, src_rows, nt_out);
 }
 
 template <int FMT>

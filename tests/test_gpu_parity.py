@@ -178,6 +178,12 @@ COL_CASES = [
     # long groups (many row blocks per group and strip), alone and next to short ones
     (40000, 24, [40000]),
     (40000, 40, [100, 700, 39000, 40000]),
+    # one block per (group, 16-column strip): a group longer than the 8192 rows a block holds
+    # (walked twice by its block), one exactly at the limit from an unaligned start, empty and
+    # 1-row groups
+    (12000, 1024, [5, 5, 17, 33, 40, 41, 60, 80, 100, 130, 200, 300, 301, 302, 310, 320, 9321,
+                   12000]),
+    (9000, 1024, [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 8200, 9000]),
 ]
 
 
