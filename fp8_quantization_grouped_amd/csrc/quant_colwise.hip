@@ -326,6 +326,123 @@ __global__ __launch_bounds__(256) void colwise_cast_kernel(
     }
 }
 
+// ------------------------------------------------------------------ long groups, one block each
+// For long groups (the expert weights: K rows per expert) one 1024-thread block owns a whole
+// (group, 64-column strip): it streams the strip once for the column maxima (lanes keep packed
+// maxima, then lane shuffles and LDS across the 16 waves; no atomics, no workspace), turns them
+// into scales, and streams it again to cast, transposing 1024-row tiles through LDS so that each
+// column is written in 1 KB runs.  One block runs per CU (the LDS tile is padded past 80 KB), so
+// the strips being walked at any moment total ~256 x 0.9 MB and the second read of a strip is
+// served by the 256 MB last-level cache.  Measured on the 32 x 7168 x 2048 weights: 410 us with
+// one block per CU, 497 us when two fit; streaming loads on the second read 388 us.
+// Lane layout as in the two-pass kernels: lane (o = t & 7, qd = t >> 3) holds rows
+// r0 + 8*qd + i (i < 8) x columns c0 + 8*o .. +7; a tile is 1024 rows x 64 columns.
+constexpr int CL_TR = 1024, CL_STR = CL_TR + 272;  // > 80 KB of LDS: one block per CU
+
+template <int FMT, bool VEC_OUT>
+__global__ __launch_bounds__(1024) void colwise_long_kernel(
+    const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ld_x,
+    const int32_t* __restrict__ offsets, int G, uint8_t* __restrict__ qt, int64_t ld_qt,
+    float* __restrict__ scales) {
+    const int t = threadIdx.x, o = t & 7, qd = t >> 3, lane = t & 63, wave = t >> 6;
+    const int64_t ST = (C + CW_TC - 1) / CW_TC;
+    const int g = (int)(blockIdx.x / ST);
+    const int64_t c0 = (int64_t)(blockIdx.x % ST) * CW_TC;
+    const int64_t c = c0 + 8 * o;
+    // the group's rows, clamped into [0, R] so that any offsets content keeps accesses in range
+    int64_t gs = g == 0 ? 0 : (int64_t)offsets[g - 1];
+    int64_t ge = offsets[g];
+    gs = gs < 0 ? 0 : (gs > R ? R : gs);
+    ge = ge < gs ? gs : (ge > R ? R : ge);
+    __shared__ uint32_t red[16][8][4];
+    __shared__ __align__(16) float scl[CW_TC];
+    __shared__ __align__(16) uint8_t tile[CW_TC * CL_STR];
+    const int64_t tb = gs & ~(int64_t)(CL_TR - 1);  // tiles start at multiples of 1024 rows
+
+    // rows outside the group load as zero; the second (last) read of a row streams (NT)
+    auto load = [&](int64_t r0, uint4 v[8], bool nt) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int64_t r = r0 + 8 * qd + i;
+            const uint16_t* px = x + r * ld_x + c;
+            v[i] = (r >= gs && r < ge && c < C)
+                       ? (nt ? ld_nt16(px) : *reinterpret_cast<const uint4*>(px))
+                       : make_uint4(0, 0, 0, 0);
+        }
+    };
+    // pass 1: column maxima of the group
+    uint32_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
+    for (int64_t r0 = tb; r0 < ge; r0 += CL_TR) {
+        uint4 v[8];
+        load(r0, v, false);
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            m0 = pk_max_u16(m0, mag2(v[i].x));
+            m1 = pk_max_u16(m1, mag2(v[i].y));
+            m2 = pk_max_u16(m2, mag2(v[i].z));
+            m3 = pk_max_u16(m3, mag2(v[i].w));
+        }
+    }
+#pragma unroll
+    for (int sh = 8; sh < 64; sh <<= 1) {
+        m0 = pk_max_u16(m0, (uint32_t)__shfl_xor((int)m0, sh, 64));
+        m1 = pk_max_u16(m1, (uint32_t)__shfl_xor((int)m1, sh, 64));
+        m2 = pk_max_u16(m2, (uint32_t)__shfl_xor((int)m2, sh, 64));
+        m3 = pk_max_u16(m3, (uint32_t)__shfl_xor((int)m3, sh, 64));
+    }
+    if (lane < 8) {
+        red[wave][lane][0] = m0;
+        red[wave][lane][1] = m1;
+        red[wave][lane][2] = m2;
+        red[wave][lane][3] = m3;
+    }
+    __syncthreads();
+    if (t < CW_TC) {
+        const int oo = t >> 3, d = (t & 7) >> 1, half = t & 1;
+        uint32_t mm = 0;
+#pragma unroll
+        for (int w = 0; w < 16; w++) mm = pk_max_u16(mm, red[w][oo][d]);
+        const uint32_t bits = half ? (mm >> 16) : (mm & 0xFFFFu);
+        const float sc = scale_from_amax<FMT>(__uint_as_float(bits << 16));
+        if (c0 + t < C) scales[(int64_t)g * C + c0 + t] = sc;
+        scl[t] = sc * Fmt<FMT>::mult;
+    }
+    __syncthreads();
+    const float4 sa = *reinterpret_cast<const float4*>(&scl[8 * o]);
+    const float4 sb = *reinterpret_cast<const float4*>(&scl[8 * o + 4]);
+    const float sj[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+    // pass 2: cast, transpose through LDS, write 16-byte chunks of each column's run
+    for (int64_t r0 = tb; r0 < ge; r0 += CL_TR) {
+        uint4 v[8];
+        load(r0, v, true);
+        __syncthreads();  // the previous tile's bytes have been stored
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            float y[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) y[i] = cw_elem(v[i], j) * sj[j];
+            *reinterpret_cast<uint2*>(&tile[(8 * o + j) * CL_STR + 8 * qd]) =
+                make_uint2(enc4<FMT>(y[0], y[1], y[2], y[3]), enc4<FMT>(y[4], y[5], y[6], y[7]));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kq = 0; kq < 4; kq++) {
+            const int ch = t + 1024 * kq;
+            const int col = ch >> 6, seg = ch & 63;  // 64 chunks of 16 rows per column
+            const int64_t cc = c0 + col, r = r0 + 16 * seg;
+            if (cc >= C || r + 16 <= gs || r >= ge) continue;
+            const uint8_t* src = &tile[col * CL_STR + 16 * seg];
+            uint8_t* dst = qt + cc * ld_qt + r;
+            if (VEC_OUT && r >= gs && r + 16 <= ge) {
+                st_nt16(dst, *reinterpret_cast<const uint4*>(src));
+            } else {
+                for (int bb = 0; bb < 16; bb++)
+                    if (r + bb >= gs && r + bb < ge) dst[bb] = src[bb];
+            }
+        }
+    }
+}
+
 template <int FMT, bool VEC, bool VEC_OUT>
 static void launch_cast(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x,
                         const int32_t* offsets, int G, const uint32_t* ws, uint8_t* qt,
@@ -347,6 +464,21 @@ static fp8q_status_t colwise_run(const uint16_t* x, int64_t R, int64_t C, int64_
                                  float* s, uint32_t* ws, hipStream_t stream) {
     const bool vec = (C % 8 == 0) && (ld_x % 8 == 0) && fp8q_aligned(x, 16);
     const bool vec_out = (ld_qt % 16 == 0) && fp8q_aligned(qt, 16);
+    // Long groups (average at least 4096 rows, e.g. expert weights) with enough (group, strip)
+    // pairs to fill the device: one block per pair, no workspace.
+    const int64_t strips = (C + CW_TC - 1) / CW_TC;
+    if (vec && R >= 4096 * (int64_t)G && (int64_t)G * strips >= 512 &&
+        (int64_t)G * strips <= 0x7FFFFFFFLL) {
+        const dim3 grid((unsigned)(G * strips));
+        if (vec_out)
+            colwise_long_kernel<FMT, true><<<grid, dim3(1024), 0, stream>>>(
+                x, R, C, ld_x, offsets, G, qt, ld_qt, s);
+        else
+            colwise_long_kernel<FMT, false><<<grid, dim3(1024), 0, stream>>>(
+                x, R, C, ld_x, offsets, G, qt, ld_qt, s);
+        FP8Q_CHECK_LAUNCH();
+        return FP8Q_OK;
+    }
     const int64_t n = (int64_t)G * C;
     int64_t zb = (n + 255) / 256;
     if (zb > 4096) zb = 4096;

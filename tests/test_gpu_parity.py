@@ -9,6 +9,8 @@ tails, empty groups and groups that start or end on tile boundaries.
 """
 from __future__ import annotations
 
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -197,6 +199,29 @@ def test_colwise_grouped_parity(fq, fmt, case):
     oqt, os_ = oracle.quant_colwise_grouped(x, off, fmt)
     assert np.array_equal(s.cpu().numpy(), os_)
     assert np.array_equal(qt.cpu().numpy(), oqt)
+
+
+@functools.lru_cache(maxsize=2)
+def _long_group_case(fmt):
+    x = workloads.make_matrix(77, 20000, 8192, 1.0, 0.01)
+    off = np.array([4999, 4999, 13001, 20000], np.int32)
+    return (x, off) + tuple(oracle.quant_colwise_grouped(x, off, fmt))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("pad", [0, 5])
+def test_colwise_long_groups(fq, fmt, pad):
+    """Groups averaging >= 4096 rows over >= 512 (group, 64-column strip) pairs: one block per
+    pair walks its strip twice.  Unaligned group edges, an empty group, and an output stride
+    that is not a multiple of 16 (pad 5) for the byte-wise store path."""
+    rows, cols = 20000, 8192
+    x, off, oqt, os_ = _long_group_case(fmt)
+    buf = torch.full((cols, rows + pad), 0xCD, dtype=torch.uint8, device=DEV)
+    qt, s = fq.fp8_quant_colwise_grouped(dev_bf16(x), dev_i32(off), fmt, q_t=buf[:, :rows])
+    b = buf.cpu().numpy()
+    assert np.array_equal(s.cpu().numpy(), os_)
+    assert np.array_equal(b[:, :rows], oqt)
+    assert np.all(b[:, rows:] == 0xCD)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
