@@ -141,6 +141,10 @@ class Step:
             # data gradient: dY and W quantized rowwise along N (the contraction), dX bf16 [M, K]
             self.buf.update(dyq=e(M, N), sdyr=e(M, dt=f32), wqn=e(E * K, N), swk=e(E * K, dt=f32),
                             dx=e(M, K, dt=bf))
+            # both weight layouts in one call (quantized once per optimizer step)
+            self.buf.update(dwr=e(E * K, N), dwrs=e(E * K, dt=f32), dwt=e(N, E * K),
+                            dwts=e(E, N, dt=f32),
+                            ws_dual=e(max(256, fq.fp8_quant_weights_dual_workspace_size(E, K, N))))
         if "mx" in d["ops"]:
             self.buf.update(mxq=e(M, K), mxe=e(M, K // 32), mxwt=e(N, E * K),
                             mxwe=e(N, E * K // 32), ymx=e(M, N, dt=bf))
@@ -178,6 +182,8 @@ class Step:
             self.gemm_bytes["gemm_dgrad"] = M * N + E * K * N + M * K * 2 + M * 4 + E * K * 4
             self.bytes["quant_rowwise_dy"] = M * N * 3 + M * 4
             self.bytes["quant_rowwise_w"] = E * K * N * 3 + E * K * 4
+            # algorithmic: W read once, both FP8 layouts written, both scale sets
+            self.bytes["quant_weights_dual"] = E * K * N * 4 + E * K * 4 + E * N * 4
         if "mx" in d["ops"]:
             self.flops["gemm_mx"] = 2.0 * M * N * K
             self.gemm_bytes["gemm_mx"] = (M * K + E * N * K + M * N * 2 + M * K // 32
@@ -227,6 +233,9 @@ class Step:
                 ("gemm_dgrad", lambda: fq.fp8_grouped_gemm(
                     fq.GEMM_FWD_MGROUPED, fmt, b["dyq"], b["sdyr"], b["wqn"], b["swk"],
                     d["offsets"], M, K, N, ldb=N, b_group_stride=K * N, c=b["dx"])),
+                ("quant_weights_dual", lambda: fq.fp8_quant_weights_dual(
+                    d["w"], E, fmt, q_rows=b["dwr"], s_rows=b["dwrs"], q_t=b["dwt"],
+                    s_cols=b["dwts"], workspace=b["ws_dual"])),
             ]
         if "mx" in d["ops"]:
             seq += [

@@ -36,6 +36,9 @@ SIGNATURES = {
     "fp8_quant_colwise_grouped_workspace_size": (_SZ, [_I64, _I64, _I32]),
     "fp8_quant_colwise_grouped": (_I, [_P, _I64, _I64, _I64, _P, _I32, _I, _P, _I64, _P, _P, _SZ,
                                        _P]),
+    "fp8_quant_weights_dual_workspace_size": (_SZ, [_I64, _I64, _I64]),
+    "fp8_quant_weights_dual": (_I, [_P, _I64, _I64, _I64, _I64, _I, _P, _I64, _P, _P, _I64, _P, _P,
+                                    _SZ, _P]),
     "fp8_grouped_gemm": (_I, [_I, _I, _P, _I64, _P, _P, _I64, _I64, _P, _P, _I32, _I64, _I64,
                               _I64, _P, _I64, _P]),
     "fp8_mx_quant_rowwise": (_I, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P]),
@@ -148,6 +151,43 @@ def fp8_quant_colwise_grouped(x: torch.Tensor, offsets: torch.Tensor, fmt: int,
                                          _ptr(workspace), workspace.numel(), _stream(x))
     _check("fp8_quant_colwise_grouped", st)
     return q_t, scales
+
+
+def fp8_quant_weights_dual_workspace_size(experts: int, K: int, N: int) -> int:
+    return int(lib().fp8_quant_weights_dual_workspace_size(experts, K, N))
+
+
+def fp8_quant_weights_dual(w: torch.Tensor, experts: int, fmt: int,
+                           q_rows: torch.Tensor | None = None,
+                           s_rows: torch.Tensor | None = None,
+                           q_t: torch.Tensor | None = None, s_cols: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None):
+    """Expert weights w: bf16 [experts*K, N] in both layouts at once.  Returns
+    (q_rows uint8 [experts*K, N], s_rows float32 [experts*K]) as fp8_quant_rowwise would and
+    (q_t uint8 [N, experts*K], s_cols float32 [experts, N]) as fp8_quant_colwise_grouped with
+    offsets K, 2K, .. would."""
+    _dev(w, "w")
+    assert w.dtype == torch.bfloat16 and w.dim() == 2 and w.stride(1) == 1
+    rows, N = w.shape
+    assert experts > 0 and rows % experts == 0
+    K = rows // experts
+    if q_rows is None:
+        q_rows = torch.empty((rows, N), dtype=torch.uint8, device=w.device)
+    if s_rows is None:
+        s_rows = torch.empty((rows,), dtype=torch.float32, device=w.device)
+    if q_t is None:
+        q_t = torch.empty((N, rows), dtype=torch.uint8, device=w.device)
+    if s_cols is None:
+        s_cols = torch.empty((experts, N), dtype=torch.float32, device=w.device)
+    need = fp8_quant_weights_dual_workspace_size(experts, K, N)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=w.device)
+    st = lib().fp8_quant_weights_dual(_ptr(w), experts, K, N, w.stride(0), fmt, _ptr(q_rows),
+                                      q_rows.stride(0), _ptr(s_rows), _ptr(q_t), q_t.stride(0),
+                                      _ptr(s_cols), _ptr(workspace), workspace.numel(),
+                                      _stream(w))
+    _check("fp8_quant_weights_dual", st)
+    return (q_rows, s_rows), (q_t, s_cols)
 
 
 def fp8_grouped_gemm(mode: int, fmt: int, a: torch.Tensor, a_scales: torch.Tensor,

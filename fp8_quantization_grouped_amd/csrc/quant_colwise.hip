@@ -337,10 +337,15 @@ __global__ __launch_bounds__(256) void colwise_cast_kernel(
 // one block per CU, 497 us when two fit; streaming loads on the second read 388 us.
 // Lane layout as in the two-pass kernels: lane (o = t & 7, qd = t >> 3) holds rows
 // r0 + 8*qd + i (i < 8) x columns c0 + 8*o .. +7; a tile is 1024 rows x 64 columns.
-constexpr int CL_TR = 1024, CL_STR = CL_TR + 272;  // > 80 KB of LDS: one block per CU
+// LDS bytes per transposed column: 1024-row tiles are padded past 80 KB in all (one block per
+// CU); smaller tiles let several blocks share a CU.
+template <int TR>
+struct LongTile {
+    static constexpr int STR = TR == 1024 ? TR + 272 : TR + 16;
+};
 
-template <int FMT, bool VEC_OUT>
-__global__ __launch_bounds__(1024) void colwise_long_kernel(
+template <int FMT, bool VEC_OUT, int TR>
+__global__ __launch_bounds__(TR) void colwise_long_kernel(
     const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ld_x,
     const int32_t* __restrict__ offsets, int G, uint8_t* __restrict__ qt, int64_t ld_qt,
     float* __restrict__ scales) {
@@ -354,7 +359,8 @@ __global__ __launch_bounds__(1024) void colwise_long_kernel(
     int64_t ge = offsets[g];
     gs = gs < 0 ? 0 : (gs > R ? R : gs);
     ge = ge < gs ? gs : (ge > R ? R : ge);
-    __shared__ uint32_t red[16][8][4];
+    constexpr int CL_TR = TR, CL_STR = LongTile<TR>::STR, NW = TR / 64;
+    __shared__ uint32_t red[NW][8][4];
     __shared__ __align__(16) float scl[CW_TC];
     __shared__ __align__(16) uint8_t tile[CW_TC * CL_STR];
     const int64_t tb = gs & ~(int64_t)(CL_TR - 1);  // tiles start at multiples of 1024 rows
@@ -401,7 +407,7 @@ __global__ __launch_bounds__(1024) void colwise_long_kernel(
         const int oo = t >> 3, d = (t & 7) >> 1, half = t & 1;
         uint32_t mm = 0;
 #pragma unroll
-        for (int w = 0; w < 16; w++) mm = pk_max_u16(mm, red[w][oo][d]);
+        for (int w = 0; w < NW; w++) mm = pk_max_u16(mm, red[w][oo][d]);
         const uint32_t bits = half ? (mm >> 16) : (mm & 0xFFFFu);
         const float sc = scale_from_amax<FMT>(__uint_as_float(bits << 16));
         if (c0 + t < C) scales[(int64_t)g * C + c0 + t] = sc;
@@ -427,8 +433,8 @@ __global__ __launch_bounds__(1024) void colwise_long_kernel(
         __syncthreads();
 #pragma unroll
         for (int kq = 0; kq < 4; kq++) {
-            const int ch = t + 1024 * kq;
-            const int col = ch >> 6, seg = ch & 63;  // 64 chunks of 16 rows per column
+            const int ch = t + TR * kq;
+            const int col = ch / (TR / 16), seg = ch % (TR / 16);  // TR/16 chunks per column
             const int64_t cc = c0 + col, r = r0 + 16 * seg;
             if (cc >= C || r + 16 <= gs || r >= ge) continue;
             const uint8_t* src = &tile[col * CL_STR + 16 * seg];
@@ -458,6 +464,118 @@ static void launch_cast(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x,
             x, R, C, ld_x, offsets, G, ws, qt, ld_qt, s);
 }
 
+// ------------------------------------------------------------------ weights in both layouts
+// Pass 1 (wdual_rows_kernel): one 256-thread block per 64 rows of one expert; wave w quantizes
+// rows w, w+4, .. (16 rows, one at a time, the next row's loads in flight) exactly as
+// fp8_quant_rowwise does: lane chunk j is columns 8*(lane + 64j) .. +7, the row maximum is a
+// wave reduction, then scale, cast and 8-byte stores.  Each lane also keeps the maxima of its
+// columns over its rows; the 4 waves combine them in LDS at the end and the block stores its
+// 64-row column maxima as bf16 magnitude bits per (block, column): plain stores, no atomics.
+// wdual_colmax_kernel reduces them per (expert, column) into the maxima layout of the colwise
+// cast pass (and writes the offsets K, 2K, ..), which then runs unchanged.
+constexpr int WD_RB = 64;  // rows per block of pass 1
+constexpr int WD_NV = 4;   // 16-byte chunks per lane: N <= 64 * 8 * WD_NV = 2048
+constexpr int WD_NMAX = 64 * 8 * WD_NV;
+
+template <int FMT>
+__global__ __launch_bounds__(256) void wdual_rows_kernel(
+    const uint16_t* __restrict__ w, int64_t K, int64_t N, int64_t ld_w, int64_t nb,
+    uint8_t* __restrict__ qr, int64_t ld_qr, float* __restrict__ s_rows,
+    uint16_t* __restrict__ part, bool nt_out) {
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t e = blockIdx.x / nb, b = blockIdx.x % nb;
+    const int64_t kr0 = b * WD_RB + wave;  // this wave's first row within the expert
+    __shared__ __align__(16) uint32_t cred[4][64 * WD_NV][4];
+    auto load = [&](int64_t kr, uint4 v[WD_NV]) {
+#pragma unroll
+        for (int j = 0; j < WD_NV; j++) {
+            const int64_t col = 8 * (int64_t)(lane + 64 * j);
+            v[j] = (kr < K && col < N) ? ld_nt16(w + (e * K + kr) * ld_w + col)
+                                       : make_uint4(0, 0, 0, 0);
+        }
+    };
+    uint32_t cm[WD_NV][4];
+#pragma unroll
+    for (int j = 0; j < WD_NV; j++) cm[j][0] = cm[j][1] = cm[j][2] = cm[j][3] = 0u;
+    uint4 v[WD_NV], vn[WD_NV];
+    load(kr0, v);
+    for (int i = 0; i < WD_RB / 4; i++) {
+        const int64_t kr = kr0 + 4 * i;
+        if (i + 1 < WD_RB / 4) load(kr + 4, vn);
+        if (kr < K) {  // wave-uniform
+            uint32_t m = 0;
+#pragma unroll
+            for (int j = 0; j < WD_NV; j++) {
+                m = pk_max_u16(m, pk_max_u16(pk_max_u16(mag2(v[j].x), mag2(v[j].y)),
+                                             pk_max_u16(mag2(v[j].z), mag2(v[j].w))));
+                cm[j][0] = pk_max_u16(cm[j][0], mag2(v[j].x));
+                cm[j][1] = pk_max_u16(cm[j][1], mag2(v[j].y));
+                cm[j][2] = pk_max_u16(cm[j][2], mag2(v[j].z));
+                cm[j][3] = pk_max_u16(cm[j][3], mag2(v[j].w));
+            }
+            const uint32_t amax = wave_max_u32(hmax16(m));
+            const float sc = scale_from_amax<FMT>(__uint_as_float(amax << 16));
+            if (lane == 0) s_rows[e * K + kr] = sc;
+            const float sm = sc * Fmt<FMT>::mult;
+#pragma unroll
+            for (int j = 0; j < WD_NV; j++) {
+                const int64_t col = 8 * (int64_t)(lane + 64 * j);
+                if (col >= N) continue;
+                const uint32_t w0 = enc4<FMT>(bf16_lo(v[j].x) * sm, bf16_hi(v[j].x) * sm,
+                                              bf16_lo(v[j].y) * sm, bf16_hi(v[j].y) * sm);
+                const uint32_t w1 = enc4<FMT>(bf16_lo(v[j].z) * sm, bf16_hi(v[j].z) * sm,
+                                              bf16_lo(v[j].w) * sm, bf16_hi(v[j].w) * sm);
+                uint8_t* dst = qr + (e * K + kr) * ld_qr + col;
+                if (nt_out) st_nt8(dst, w0, w1);  // block-uniform
+                else *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < WD_NV; j++) v[j] = vn[j];
+    }
+#pragma unroll
+    for (int j = 0; j < WD_NV; j++)
+        *reinterpret_cast<uint4*>(&cred[wave][lane + 64 * j][0]) =
+            make_uint4(cm[j][0], cm[j][1], cm[j][2], cm[j][3]);
+    __syncthreads();
+    // chunk q = t holds columns 8q .. 8q+7 (64 * WD_NV = 256 chunks)
+    if (8 * (int64_t)t < N) {
+        uint32_t mm[4];
+#pragma unroll
+        for (int d = 0; d < 4; d++)
+            mm[d] = pk_max_u16(pk_max_u16(cred[0][t][d], cred[1][t][d]),
+                               pk_max_u16(cred[2][t][d], cred[3][t][d]));
+        *reinterpret_cast<uint4*>(part + (e * nb + b) * N + 8 * (int64_t)t) =
+            make_uint4(mm[0], mm[1], mm[2], mm[3]);
+    }
+}
+
+__global__ void wdual_colmax_kernel(const uint16_t* __restrict__ part, int64_t nb, int64_t E,
+                                    int64_t N, int64_t K, uint32_t* __restrict__ amax,
+                                    int32_t* __restrict__ offs) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < E) offs[i] = (int32_t)((i + 1) * K);  // host: E * K < 2^31
+    if (i >= E * N) return;
+    const int64_t e = i / N, n = i % N;
+    uint32_t m = 0;
+    for (int64_t b = 0; b < nb; b++) {
+        const uint32_t u = part[(e * nb + b) * N + n];
+        m = u > m ? u : m;
+    }
+    amax[i] = m;
+}
+
+// Workspace: column maxima [E][N] u32 | offsets [E] int32 | block maxima [E*nb][N] u16, each
+// part 256-byte aligned.
+static inline void wdual_layout(int64_t E, int64_t K, int64_t N, size_t& o_offs, size_t& o_part,
+                                size_t& total) {
+    auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+    const int64_t nb = (K + WD_RB - 1) / WD_RB;
+    o_offs = up((size_t)E * (size_t)N * 4);
+    o_part = o_offs + up((size_t)E * 4);
+    total = o_part + up((size_t)E * (size_t)nb * (size_t)N * 2);
+}
+
 template <int FMT>
 static fp8q_status_t colwise_run(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x,
                                  const int32_t* offsets, int G, uint8_t* qt, int64_t ld_qt,
@@ -471,10 +589,10 @@ static fp8q_status_t colwise_run(const uint16_t* x, int64_t R, int64_t C, int64_
         (int64_t)G * strips <= 0x7FFFFFFFLL) {
         const dim3 grid((unsigned)(G * strips));
         if (vec_out)
-            colwise_long_kernel<FMT, true><<<grid, dim3(1024), 0, stream>>>(
+            colwise_long_kernel<FMT, true, 1024><<<grid, dim3(1024), 0, stream>>>(
                 x, R, C, ld_x, offsets, G, qt, ld_qt, s);
         else
-            colwise_long_kernel<FMT, false><<<grid, dim3(1024), 0, stream>>>(
+            colwise_long_kernel<FMT, false, 1024><<<grid, dim3(1024), 0, stream>>>(
                 x, R, C, ld_x, offsets, G, qt, ld_qt, s);
         FP8Q_CHECK_LAUNCH();
         return FP8Q_OK;
@@ -544,4 +662,63 @@ extern "C" fp8q_status_t fp8_quant_colwise_grouped(const uint16_t* x, int64_t ro
                                               scales, ws, stream);
     return fp8q::colwise_run<FP8Q_E4M3FNUZ>(x, rows, cols, ld_x, offsets, groups, q_t, ld_qt,
                                             scales, ws, stream);
+}
+
+extern "C" size_t fp8_quant_weights_dual_workspace_size(int64_t experts, int64_t K, int64_t N) {
+    if (experts < 0 || K < 0 || N < 0) return 0;
+    size_t a, b, total;
+    fp8q::wdual_layout(experts, K, N, a, b, total);
+    return total < 256 ? 256 : total;
+}
+
+extern "C" fp8q_status_t fp8_quant_weights_dual(const uint16_t* w, int64_t experts, int64_t K,
+                                                int64_t N, int64_t ld_w, fp8q_format_t fmt,
+                                                uint8_t* q_rows, int64_t ld_qr, float* s_rows,
+                                                uint8_t* q_t, int64_t ld_qt, float* s_cols,
+                                                void* workspace, size_t workspace_bytes,
+                                                hipStream_t stream) {
+    if (experts < 0 || K < 0 || N < 0 || ld_w < N || ld_qr < N || ld_qt < experts * K ||
+        !fp8q_fmt_ok(fmt))
+        return FP8Q_ERR_INVALID_ARG;
+    if (experts == 0 || K == 0 || N == 0) return FP8Q_OK;
+    if (!w || !q_rows || !s_rows || !q_t || !s_cols) return FP8Q_ERR_INVALID_ARG;
+    const int64_t nb = (K + fp8q::WD_RB - 1) / fp8q::WD_RB;
+    if (N > fp8q::WD_NMAX || N % 8 || ld_w % 8 || ld_qr % 8 || !fp8q_aligned(w, 16) ||
+        !fp8q_aligned(q_rows, 8) || experts * nb > 0x7FFFFFFFLL ||
+        experts * K > 0x7FFFFFFFLL || experts > 0x7FFFFFFFLL / 256 ||
+        (experts * K + fp8q::CW_TR - 1) / fp8q::CW_TR > 0x7FFFFFFFLL ||
+        (N + fp8q::CW_TC - 1) / fp8q::CW_TC > 65535)
+        return FP8Q_ERR_UNSUPPORTED;
+    size_t o_offs, o_part, total;
+    fp8q::wdual_layout(experts, K, N, o_offs, o_part, total);
+    if (!workspace || workspace_bytes < total) return FP8Q_ERR_WORKSPACE;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    uint32_t* amax = reinterpret_cast<uint32_t*>(ws);
+    int32_t* offs = reinterpret_cast<int32_t*>(ws + o_offs);
+    uint16_t* part = reinterpret_cast<uint16_t*>(ws + o_part);
+    const bool nt_out = (double)experts * (double)K * (double)ld_qr > fp8q::kStreamBytes;
+    const int64_t R = experts * K;
+    const bool vec_out = (ld_qt % 16 == 0) && fp8q_aligned(q_t, 16);
+    const int64_t nred = (experts * N > experts ? experts * N : experts);
+    if (fmt == FP8Q_E4M3FN)
+        fp8q::wdual_rows_kernel<FP8Q_E4M3FN><<<dim3((unsigned)(experts * nb)), dim3(256), 0, stream>>>(
+            w, K, N, ld_w, nb, q_rows, ld_qr, s_rows, part, nt_out);
+    else
+        fp8q::wdual_rows_kernel<FP8Q_E4M3FNUZ><<<dim3((unsigned)(experts * nb)), dim3(256), 0, stream>>>(
+            w, K, N, ld_w, nb, q_rows, ld_qr, s_rows, part, nt_out);
+    fp8q::wdual_colmax_kernel<<<dim3((unsigned)((nred + 255) / 256)), dim3(256), 0, stream>>>(
+        part, nb, experts, N, K, amax, offs);
+    if (fmt == FP8Q_E4M3FN) {
+        if (vec_out)
+            fp8q::launch_cast<FP8Q_E4M3FN, true, true>(w, R, N, ld_w, offs, (int)experts, amax, q_t, ld_qt, s_cols, stream);
+        else
+            fp8q::launch_cast<FP8Q_E4M3FN, true, false>(w, R, N, ld_w, offs, (int)experts, amax, q_t, ld_qt, s_cols, stream);
+    } else {
+        if (vec_out)
+            fp8q::launch_cast<FP8Q_E4M3FNUZ, true, true>(w, R, N, ld_w, offs, (int)experts, amax, q_t, ld_qt, s_cols, stream);
+        else
+            fp8q::launch_cast<FP8Q_E4M3FNUZ, true, false>(w, R, N, ld_w, offs, (int)experts, amax, q_t, ld_qt, s_cols, stream);
+    }
+    FP8Q_CHECK_LAUNCH();
+    return FP8Q_OK;
 }

@@ -128,6 +128,30 @@ fp8q_status_t fp8_quant_colwise_grouped(const uint16_t* x, int64_t rows, int64_t
                                         float* scales, void* workspace, size_t workspace_bytes,
                                         hipStream_t stream);
 
+/* Expert weights in both layouts at once, for quantizing them once per optimizer step and
+ * reusing the bytes across micro-batches (the forward reads W^T per expert with one scale per
+ * (expert, output column); the data gradient reads W along N with one scale per (expert, k)).
+ * Same results as the two separate calls, bit for bit:
+ *   q_rows, s_rows = fp8_quant_rowwise(w)                            (scales along N)
+ *   q_t, s_cols    = fp8_quant_colwise_grouped(w, offsets K, 2K, ..) (scales along K)
+ * but W is read twice instead of three times and no atomics are used: the rowwise pass also
+ * writes each 64-row block's column maxima, which a small kernel reduces per expert before the
+ * colwise cast pass (ai-radar.it, "Il guadagno vero e' nel movimento dei dati": fewer passes
+ * over HBM; fosswire.org, "What Primus adds for MoE training on MI355X": FP8 expert weights).
+ *   w        bf16 [experts*K][ld_w], ld_w >= N; expert e is rows e*K .. e*K+K-1
+ *   q_rows   u8 [experts*K][ld_qr], ld_qr >= N      s_rows fp32 [experts*K]
+ *   q_t      u8 [N][ld_qt], ld_qt >= experts*K      s_cols fp32 [experts][N]
+ *   workspace >= fp8_quant_weights_dual_workspace_size(experts, K, N) bytes, any content.
+ * Limits (FP8Q_ERR_UNSUPPORTED, nothing launched): N <= 2048, N, ld_w and ld_qr multiples of 8,
+ * w 16-byte and q_rows 8-byte aligned, experts * ceil(K/64) < 2^31.  experts == 0, K == 0 or
+ * N == 0 is a no-op. */
+size_t fp8_quant_weights_dual_workspace_size(int64_t experts, int64_t K, int64_t N);
+fp8q_status_t fp8_quant_weights_dual(const uint16_t* w, int64_t experts, int64_t K, int64_t N,
+                                     int64_t ld_w, fp8q_format_t fmt, uint8_t* q_rows,
+                                     int64_t ld_qr, float* s_rows, uint8_t* q_t, int64_t ld_qt,
+                                     float* s_cols, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
 /* Scaled FP8 grouped GEMM with fp32 accumulation on FP8 MFMA and dequantization fused into
  * the epilogue; bf16 output, rounded to nearest even (latestnews.news third paragraph: grouped
  * GEMM for MoE on ROCm; fosswire.org "What Primus adds for MoE training on MI355X": FP8 grouped

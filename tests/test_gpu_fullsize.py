@@ -96,6 +96,23 @@ def test_colwise_full_dsv3_weights(fq, dsv3_fwd):
     assert np.array_equal(qt.cpu().numpy(), oqt)
 
 
+def test_weights_dual_full_dsv3(fq, dsv3_fwd):
+    """Both weight layouts of the 32 x 7168 x 2048 experts in one call; three experts (first,
+    middle, last) compared with the oracle in full, rows and columns."""
+    d = dsv3_fwd
+    E, K, N, w = d["E"], d["K"], d["N"], d["w"]
+    (qr, sr), (qt, sc) = fq.fp8_quant_weights_dual(workloads.to_torch_bf16(w, DEV), E, FN)
+    qr, sr, qt, sc = (t.cpu().numpy() for t in (qr, sr, qt, sc))
+    for e in (0, 13, E - 1):
+        we = w[e * K:(e + 1) * K]
+        oq, os_ = oracle.quant_rowwise(we, FN)
+        assert np.array_equal(sr[e * K:(e + 1) * K], os_)
+        assert np.array_equal(qr[e * K:(e + 1) * K], oq)
+        oqt, osc = oracle.quant_colwise_grouped(we, np.array([K], np.int32), FN)
+        assert np.array_equal(sc[e], osc[0])
+        assert np.array_equal(qt[:, e * K:(e + 1) * K], oqt)
+
+
 @pytest.mark.parametrize("which", ["x", "dy"])
 def test_colwise_full_dsv3_wgrad_operands(fq, dsv3_bwd, which):
     d = dsv3_bwd

@@ -263,6 +263,43 @@ def test_colwise_deterministic_across_calls(fq):
         assert np.array_equal(cur[0], ref[0]) and np.array_equal(cur[1], ref[1])
 
 
+# ----------------------------------------------------------------------------- weights, both layouts
+
+WDUAL_CASES = [
+    # experts, K, N, pad (extra elements in the rows of w, q_rows and q_t)
+    (4, 256, 512, 0),
+    (4, 200, 512, 8),    # K not a multiple of the 64-row blocks; padded strides (ld_qt 808)
+    (3, 64, 2048, 0),    # the widest N
+    (2, 130, 8, 16),     # one 8-column chunk per row
+    (1, 1, 16, 0),
+]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("case", WDUAL_CASES)
+def test_weights_dual_parity(fq, fmt, case):
+    """fp8_quant_weights_dual: the rowwise layout (scales along N) and the colwise layout
+    (scales along K per expert) in one call, each equal to the oracle bit for bit."""
+    E, K, N, pad = case
+    w = workloads.make_matrix(300 + E + K + N, E * K, N, 0.02, 0.01)
+    q_rows = torch.full((E * K, N + pad), 0xCD, dtype=torch.uint8, device=DEV)
+    q_t = torch.full((N, E * K + pad), 0xCD, dtype=torch.uint8, device=DEV)
+    (_, sr), (_, sc) = fq.fp8_quant_weights_dual(dev_bf16(w, ld=N + pad), E, fmt,
+                                                 q_rows=q_rows[:, :N], q_t=q_t[:, :E * K])
+    oq, os_ = oracle.quant_rowwise(w, fmt)
+    oqt, osc = oracle.quant_colwise_grouped(w, (np.arange(1, E + 1) * K).astype(np.int32), fmt)
+    qr_h, qt_h = q_rows.cpu().numpy(), q_t.cpu().numpy()
+    assert np.array_equal(sr.cpu().numpy(), os_) and np.array_equal(qr_h[:, :N], oq)
+    assert np.array_equal(sc.cpu().numpy(), osc) and np.array_equal(qt_h[:, :E * K], oqt)
+    assert np.all(qr_h[:, N:] == 0xCD) and np.all(qt_h[:, E * K:] == 0xCD)
+
+
+def test_weights_dual_rejects_wide_rows(fq):
+    w = torch.zeros((64, 2056), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(RuntimeError, match="status 2"):
+        fq.fp8_quant_weights_dual(w, 1, FN)
+
+
 # ----------------------------------------------------------------------------- grouped GEMM
 
 def _fwd_operands(fmt, M, K, N, E, seed):
