@@ -135,7 +135,7 @@ fp8q_status_t fp8_quant_colwise_grouped(const uint16_t* x, int64_t rows, int64_t
  *   q_rows, s_rows = fp8_quant_rowwise(w)                            (scales along N)
  *   q_t, s_cols    = fp8_quant_colwise_grouped(w, offsets K, 2K, ..) (scales along K)
  * but W is read twice instead of three times and no atomics are used: the rowwise pass also
- * writes each 64-row block's column maxima, which a small kernel reduces per expert before the
+ * writes each 128-row block's column maxima, which a small kernel reduces per expert before the
  * colwise cast pass (ai-radar.it, "Il guadagno vero e' nel movimento dei dati": fewer passes
  * over HBM; fosswire.org, "What Primus adds for MoE training on MI355X": FP8 expert weights).
  *   w        bf16 [experts*K][ld_w], ld_w >= N; expert e is rows e*K .. e*K+K-1

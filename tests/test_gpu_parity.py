@@ -268,7 +268,7 @@ def test_colwise_deterministic_across_calls(fq):
 WDUAL_CASES = [
     # experts, K, N, pad (extra elements in the rows of w, q_rows and q_t)
     (4, 256, 512, 0),
-    (4, 200, 512, 8),    # K not a multiple of the 64-row blocks; padded strides (ld_qt 808)
+    (4, 200, 512, 8),    # K not a multiple of the 128-row blocks; padded strides (ld_qt 808)
     (3, 64, 2048, 0),    # the widest N
     (2, 130, 8, 16),     # one 8-column chunk per row
     (1, 1, 16, 0),
