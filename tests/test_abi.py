@@ -119,3 +119,17 @@ def test_device_code_has_no_generic_memory_instructions():
         assert "amdgcn" in text
         hits = _build.FLAT_INSN.findall(text)
         assert not hits, (n, hits[:4])
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch):
+    """No fallback: with the HIP library absent every entry point raises, and host tensors are
+    rejected instead of being computed on the CPU."""
+    import torch
+    import fp8_quantization_grouped_amd as fq
+    x = torch.zeros((4, 8), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        fq.fp8_quant_rowwise(x, fq.E4M3FN)
+    monkeypatch.setattr(fq, "_lib", None)
+    monkeypatch.setattr(fq, "LIB_PATH", os.path.join(os.path.dirname(fq.LIB_PATH), "absent.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        fq.lib()
