@@ -561,7 +561,8 @@ __global__ void wdual_colmax_kernel(const uint16_t* __restrict__ part, int64_t n
     if (i >= E * N) return;
     const int64_t e = i / N, n = i % N;
     uint32_t m = 0;
-    for (int64_t b = 0; b < nb; b++) {
+#pragma unroll 8
+    for (int64_t b = 0; b < nb; b++) {  // unrolled: eight loads in flight
         const uint32_t u = part[(e * nb + b) * N + n];
         m = u > m ? u : m;
     }
