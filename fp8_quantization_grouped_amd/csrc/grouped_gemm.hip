@@ -11,10 +11,11 @@
 //   MX forward:          out[m,n]   = sum_kb 2^(ea+eb) sum_{k in kb} A[m,k] * B_g[n,k]
 //
 // Kernel (persistent: one block per CU):
-//   * 256x256 output tile, 128-byte contraction steps.  Plain FP8: 8 waves, two per SIMD, each
-//     owning a 128x64 sub-tile (32 v_mfma_f32_16x16x128_f8f6f4 per step, 128 accumulators per
-//     lane), so one wave's LDS reads and DMA issue overlap the other's matrix instructions.
-//     MX: 4 waves, each 128x128 (64 MFMAs per step, 256 accumulators).
+//   * 256x256 output tile, 128-byte contraction steps.  Plain FP8: 16 waves, four per SIMD,
+//     each owning a 128x32 sub-tile (16 v_mfma_f32_16x16x128_f8f6f4 per step, 64 accumulators
+//     per lane), so the other waves' matrix instructions cover one wave's LDS reads, DMA issue
+//     and waits (one wave per SIMD is bound by its own instruction issue, not by the matrix
+//     cores).  MX: 4 waves, each 128x128 (64 MFMAs per step, 256 accumulators).
 //   * Operand tiles go HBM/L2 -> LDS directly with buffer_load_dwordx4 ... lds (no staging
 //     registers), double-buffered: after the barrier of step k the loads of step k+1 are
 //     issued in 8 parts between the first half of step k's matrix instructions, and waited for
@@ -222,14 +223,14 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
     __shared__ unsigned short s_perm[MODE == MODE_WGRAD ? GMAX : 1];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    // NW = 4: each wave owns 128 x 128 of the tile; NW = 8 (two waves per SIMD): 128 x 64
-    static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+    // NW = 4: each wave owns 128 x 128 of the tile; NW = 8: 128 x 64; NW = 16: 128 x 32
+    static_assert(NW == 4 || NW == 8 || NW == 16, "4, 8 or 16 waves");
     constexpr int NT = 64 * NW;          // threads
     constexpr int NP = 32 / NW;          // operand DMA parts per wave and step (8 rows each)
-    constexpr int NJ = NW == 8 ? 4 : 8;  // 16-column blocks per wave
+    constexpr int NJ = NW == 16 ? 2 : NW == 8 ? 4 : 8;  // 16-column blocks per wave
     constexpr int WNC = 16 * NJ;         // columns per wave
     const bool row_thread = NW == 4 || wave < 4;  // threads owning one tile row (t < 256; wave-uniform)
-    const int wm = NW == 8 ? wave >> 2 : wave >> 1, wn = NW == 8 ? wave & 3 : wave & 1;
+    const int wm = wave / (NW / 2), wn = wave % (NW / 2);
     constexpr bool FNUZ = FMT == FP8Q_E4M3FNUZ;
     const int64_t tiles_per_group = (int64_t)p.nt_k * p.nt_n;
     // weight gradient: a tile's contraction starts at its group's first token rounded down to
@@ -503,7 +504,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
         const int r = row0, q = l3;
         const int row = r + 8 * i;
         const int sa = ((i & 1) << 2) | (((q >> 2) & 1) << 1) | ((q >> 1) & 1);  // swz(row)
-        const int sb = ((i & 3) << 1) | ((q >> 1) & 1);                         // swzB(row)
+        const int sb = NW == 16 ? swzB(row) : (((i & 3) << 1) | ((q >> 1) & 1));  // swzB(row)
         const int cha = (lane & 7) ^ sa, chb = (lane & 7) ^ sb;
         const int pa = P.kpos + 16 * cha, pb = P.kpos + 16 * chb;
         const bool ka = pa < P.kb_hi && pa + 16 > P.kb_lo;
@@ -620,8 +621,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
                     part(P, 2 * i);
                     part(P, 2 * i + 1);
                 }
-                if (pend && !MX && NW == 8 && i == 0) {  // 8 waves: all 4 parts up front
-#pragma unroll                                         // (measured 1-2% faster than spread)
+                if (pend && !MX && NW >= 8 && i == 0) {  // 8-16 waves: all parts up front
+#pragma unroll                                          // (measured 1-2% faster than spread)
                     for (int q = 0; q < NP; q++) part(P, q);
                 }
                 if (pend && MX && i < NP) part(P, i);  // MX: one part per row (measured faster there)
@@ -731,11 +732,11 @@ static fp8q_status_t launch_gemm(GemmArgs p, hipStream_t stream) {
     if (tiles < grid) grid = tiles;
     if (grid < 1) grid = 1;
     p.vec_store = (p.ldc % 8 == 0) && fp8q_aligned(p.c, 16);
-    // Plain FP8: 8 waves (two per SIMD, 128 x 64 each; 218-226 registers, no spills).  MX: 4
-    // waves (one per SIMD, 128 x 128 each): with two per SIMD its scale registers spill.
-    // Measured on the dsv3 step: forward 368 -> 360 us, weight gradient 606 -> 596 us, data
-    // gradient 396 -> 360 us with 8 waves; MX forward 453 -> 1606 us, so MX keeps 4.
-    constexpr int NW = MXV == MX_NONE ? 8 : 4;
+    // Plain FP8: 16 waves (four per SIMD, 128 x 32 each; 124-128 registers).  MX: 4 waves (one
+    // per SIMD, 128 x 128 each): with two per SIMD its scale registers spill (MX forward
+    // 453 -> 1606 us at 8 waves).  Measured on the dsv3 step, 4 / 8 / 16 waves: forward
+    // 368 / 352 / 328 us, weight gradient 606 / 589 / 498 us, data gradient 396 / 364 / 345 us.
+    constexpr int NW = MXV == MX_NONE ? 16 : 4;
     gemm256_kernel<FMT, MODE, MXV, NW><<<dim3((unsigned)grid), dim3(64 * NW), 0, stream>>>(p);
     FP8Q_CHECK_LAUNCH();
     return FP8Q_OK;
