@@ -275,11 +275,13 @@ def cpu_baseline(d, seconds):
     tq = time.perf_counter() - t0
     qbt, sb = oracle.quant_colwise_grouped(ws, np.array([K], np.int32), fmt)
     off = np.array([qa.shape[0]], np.int32)
-    # calibrate on 4 rows, then run a sample sized to the time budget
+    # calibrate on as many rows as the oracle has threads (fewer would leave threads idle and
+    # overstate the time per row), then run a sample sized to the time budget
+    ncal = max(4, min(1024, oracle.num_threads()))
     t0 = time.perf_counter()
-    oracle.gemm_fwd_rows(fmt, qa, sa, qbt, K, 0, sb, off, N, K, np.arange(4))
-    t4 = time.perf_counter() - t0
-    nrows = int(max(4, min(1024, 4 * seconds / max(t4, 1e-6))))
+    oracle.gemm_fwd_rows(fmt, qa, sa, qbt, K, 0, sb, off, N, K, np.arange(ncal))
+    tcal = time.perf_counter() - t0
+    nrows = int(max(4, min(1024, ncal * seconds / max(tcal, 1e-6))))
     t0 = time.perf_counter()
     oracle.gemm_fwd_rows(fmt, qa, sa, qbt, K, 0, sb, off, N, K, np.arange(nrows))
     tg = time.perf_counter() - t0
