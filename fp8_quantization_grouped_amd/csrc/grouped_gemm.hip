@@ -18,9 +18,11 @@
 //     cores).  MX: 4 waves, each 128x128 (64 MFMAs per step, 256 accumulators).
 //   * Operand tiles go HBM/L2 -> LDS directly with buffer_load_dwordx4 ... lds (no staging
 //     registers), double-buffered: after the barrier of step k the loads of step k+1 are
-//     issued in 8 parts between the first half of step k's matrix instructions, and waited for
-//     only at the top of step k+1, so one barrier per step.  Rows and chunks outside the operand are turned
-//     into out-of-range buffer offsets and read back as zeros.  Chunks are stored XOR-swizzled
+//     issued in 32 parts of 8 rows x 128 bytes per operand (16 waves: 2 parts each, before
+//     their first matrix instruction; 4 waves: 8 parts each, between the first rows of matrix
+//     instructions), and waited for only at the top of step k+1, so one barrier per step.
+//     Rows and chunks outside the operand are turned into out-of-range buffer offsets and read
+//     back as zeros.  Chunks are stored XOR-swizzled
 //     per row (swz, swzB) so that every fragment read is free of LDS bank conflicts.
 //   * The MFMA's A operand is the N-side tile and its B operand the M-side tile; N-side rows
 //     are permuted in LDS (brow) so that each lane ends with 8 consecutive output columns of
