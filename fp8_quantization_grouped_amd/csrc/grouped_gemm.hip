@@ -15,12 +15,13 @@
 //     each owning a 128x32 sub-tile (16 v_mfma_f32_16x16x128_f8f6f4 per step, 64 accumulators
 //     per lane), so the other waves' matrix instructions cover one wave's LDS reads, DMA issue
 //     and waits (one wave per SIMD is bound by its own instruction issue, not by the matrix
-//     cores).  MX: 4 waves, each 128x128 (64 MFMAs per step, 256 accumulators).
+//     cores).  MX: 8 waves, two per SIMD, each 128x64 (32 MFMAs per step, 128 accumulators).
 //   * Operand tiles go HBM/L2 -> LDS directly with buffer_load_dwordx4 ... lds (no staging
 //     registers), double-buffered: after the barrier of step k the loads of step k+1 are
 //     issued in 32 parts of 8 rows x 128 bytes per operand (16 waves: 2 parts each, before
-//     their first matrix instruction; 4 waves: 8 parts each, between the first rows of matrix
-//     instructions), and waited for only at the top of step k+1, so one barrier per step.
+//     their first matrix instruction; MX, 8 waves: 4 parts each, one between each of the first
+//     rows of matrix instructions), and waited for only at the top of step k+1, so one barrier
+//     per step.
 //     Rows and chunks outside the operand are turned into out-of-range buffer offsets and read
 //     back as zeros.  Chunks are stored XOR-swizzled
 //     per row (swz, swzB) so that every fragment read is free of LDS bank conflicts.
@@ -193,8 +194,8 @@ struct Tile {  // all extents < 2^31 (checked on the host)
 };
 
 // One block per CU runs a contiguous range of the tile sequence (persistent schedule).
-// Forward: tile t = (row-tile slot, column tile) with the column tile fastest, every tile the
-// same work; weight gradient: tiles ordered by group, each weighted by its contraction steps
+// Forward: tiles ordered by group, then column tile, then row tile (fastest), every tile the
+// same work, so a group's row tiles that share a weight tile run together; weight gradient: tiles ordered by group, each weighted by its contraction steps
 // plus one for its epilogue, so the ranges split the real work evenly whatever the group
 // sizes.  Ranges of one XCD are adjacent (blocks are dealt to XCDs round-robin), so concurrent
 // tiles share operand tiles in that XCD's L2.  The first contraction step of a block's next
@@ -347,15 +348,18 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
     auto tile_start = [&](Tile& T) -> bool {
         if (MODE == MODE_FWD) {
             if (ti >= t_end) return false;
-            const int slot = ti / p.nt_n;
-            T.n0 = (ti % p.nt_n) * GT;
-            int lo = 0, hi = p.G - 1;  // last group whose slots start at or before slot
+            // tiles of one group are ordered (column tile, row tile), row tile fastest, so the
+            // row tiles sharing a weight tile run side by side in one XCD
+            int lo = 0, hi = p.G - 1;  // last group whose tiles start at or before ti
             while (lo < hi) {
                 const int mid = (lo + hi + 1) >> 1;
-                if (s_pref[mid] <= slot) lo = mid; else hi = mid - 1;
+                if (s_pref[mid] * p.nt_n <= ti) lo = mid; else hi = mid - 1;
             }
             T.g = lo;
-            T.row_lo = (slot - s_pref[T.g]) * GT;  // relative to the group start
+            const int rt = s_pref[lo + 1] - s_pref[lo];  // row tiles of the group (> 0 here)
+            const int l = ti - s_pref[lo] * p.nt_n;
+            T.n0 = (l / rt) * GT;
+            T.row_lo = (l % rt) * GT;  // relative to the group start
             ti += bpx;
         } else {
             // round r takes tiles [r*nb, r*nb + nb) of the size order; XCD x (blocks are dealt
@@ -610,10 +614,17 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
             for (int j = 0; j < NJ; j++) {
                 const int rn = wn * WNC + brow(j, lr);
                 bf[j] = frag<true>(Bs, rn, kg, FNUZ);
-                if (MXV == MX_BYTES)
-                    sb_[j] = kb_in ? (int)((sscale[cur_st][1][rn] >> (8 * kg)) & 0xFFu) : 127;
-                if (MXV == MX_DMA)
-                    sb_[j] = kb_in ? (int)smx[((mslot * 2 + 1) * GT + rn) * 16 + msub + kg] : 127;
+                // scale bytes are read unconditionally (in-range LDS) and then selected: a
+                // conditional read becomes a branch per row, and the compiler then gathers all
+                // fragment reads ahead of the matrix instructions (registers spill)
+                if (MXV == MX_BYTES) {
+                    const int e = (int)((sscale[cur_st][1][rn] >> (8 * kg)) & 0xFFu);
+                    sb_[j] = kb_in ? e : 127;
+                }
+                if (MXV == MX_DMA) {
+                    const int e = (int)smx[((mslot * 2 + 1) * GT + rn) * 16 + msub + kg];
+                    sb_[j] = kb_in ? e : 127;
+                }
             }
             // 16 waves: a wave issuing its matrix instructions goes ahead of the other waves'
             // memory instructions (weight gradient 517 -> 510 us; forward unchanged)
@@ -632,10 +643,14 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
                 }
                 if (pend && MX && i < NP) part(P, i);  // MX: one part per row (measured faster there)
                 int sa_ = 0;
-                if (MXV == MX_BYTES)
-                    sa_ = kb_in ? (int)((sscale[cur_st][0][rm] >> (8 * kg)) & 0xFFu) : 127;
-                if (MXV == MX_DMA)
-                    sa_ = kb_in ? (int)smx[((mslot * 2 + 0) * GT + rm) * 16 + msub + kg] : 127;
+                if (MXV == MX_BYTES) {
+                    const int e = (int)((sscale[cur_st][0][rm] >> (8 * kg)) & 0xFFu);
+                    sa_ = kb_in ? e : 127;
+                }
+                if (MXV == MX_DMA) {
+                    const int e = (int)smx[((mslot * 2 + 0) * GT + rm) * 16 + msub + kg];
+                    sa_ = kb_in ? e : 127;
+                }
 #pragma unroll
                 for (int j = 0; j < NJ; j++) {
                     if (MX)
@@ -738,11 +753,12 @@ static fp8q_status_t launch_gemm(GemmArgs p, hipStream_t stream) {
     if (tiles < grid) grid = tiles;
     if (grid < 1) grid = 1;
     p.vec_store = (p.ldc % 8 == 0) && fp8q_aligned(p.c, 16);
-    // Plain FP8: 16 waves (four per SIMD, 128 x 32 each; 124-128 registers).  MX: 4 waves (one
-    // per SIMD, 128 x 128 each): with two per SIMD its scale registers spill (MX forward
-    // 453 -> 1606 us at 8 waves).  Measured on the dsv3 step, 4 / 8 / 16 waves: forward
-    // 368 / 352 / 328 us, weight gradient 606 / 589 / 498 us, data gradient 396 / 364 / 345 us.
-    constexpr int NW = MXV == MX_NONE ? 16 : 4;
+    // Plain FP8: 16 waves (four per SIMD, 128 x 32 each; 124-128 registers).  Measured on the
+    // dsv3 step, 4 / 8 / 16 waves: forward 368 / 352 / 328 us, weight gradient 606 / 589 /
+    // 498 us, data gradient 396 / 364 / 345 us.  MX: 8 waves (two per SIMD, 128 x 64 each;
+    // 256 registers): MX forward 455 -> 437 us and MX weight gradient 801 -> 739 us against 4
+    // waves; at 16 waves its DMA offsets and accumulators spill inside the loop (827 / 1267 us).
+    constexpr int NW = MXV == MX_NONE ? 16 : 8;
     gemm256_kernel<FMT, MODE, MXV, NW><<<dim3((unsigned)grid), dim3(64 * NW), 0, stream>>>(p);
     FP8Q_CHECK_LAUNCH();
     return FP8Q_OK;
