@@ -18,10 +18,9 @@
 //     cores).  MX: 8 waves, two per SIMD, each 128x64 (32 MFMAs per step, 128 accumulators).
 //   * Operand tiles go HBM/L2 -> LDS directly with buffer_load_dwordx4 ... lds (no staging
 //     registers), double-buffered: after the barrier of step k the loads of step k+1 are
-//     issued in 32 parts of 8 rows x 128 bytes per operand (16 waves: 2 parts each, before
-//     their first matrix instruction; MX, 8 waves: 4 parts each, one between each of the first
-//     rows of matrix instructions), and waited for only at the top of step k+1, so one barrier
-//     per step.
+//     issued in 32 parts of 8 rows x 128 bytes per operand (16 waves: 2 parts each; MX, 8
+//     waves: 4 parts each; all before the wave's first matrix instruction of the step), and
+//     waited for only at the top of step k+1, so one barrier per step.
 //     Rows and chunks outside the operand are turned into out-of-range buffer offsets and read
 //     back as zeros.  Chunks are stored XOR-swizzled
 //     per row (swz, swzB) so that every fragment read is free of LDS bank conflicts.
@@ -637,11 +636,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
                     part(P, 2 * i);
                     part(P, 2 * i + 1);
                 }
-                if (pend && !MX && NW >= 8 && i == 0) {  // 8-16 waves: all parts up front
+                if (pend && NW >= 8 && i == 0) {  // 8-16 waves: all parts up front
 #pragma unroll                                          // (measured 1-2% faster than spread)
                     for (int q = 0; q < NP; q++) part(P, q);
                 }
-                if (pend && MX && i < NP) part(P, i);  // MX: one part per row (measured faster there)
+                if (pend && MX && NW == 4 && i < NP) part(P, i);  // 4-wave MX: one part per row
                 int sa_ = 0;
                 if (MXV == MX_BYTES) {
                     const int e = (int)((sscale[cur_st][0][rm] >> (8 * kg)) & 0xFFu);
@@ -756,8 +755,9 @@ static fp8q_status_t launch_gemm(GemmArgs p, hipStream_t stream) {
     // Plain FP8: 16 waves (four per SIMD, 128 x 32 each; 124-128 registers).  Measured on the
     // dsv3 step, 4 / 8 / 16 waves: forward 368 / 352 / 328 us, weight gradient 606 / 589 /
     // 498 us, data gradient 396 / 364 / 345 us.  MX: 8 waves (two per SIMD, 128 x 64 each;
-    // 256 registers): MX forward 455 -> 437 us and MX weight gradient 801 -> 739 us against 4
-    // waves; at 16 waves its DMA offsets and accumulators spill inside the loop (827 / 1267 us).
+    // 256 registers, no spills with the DMA parts issued up front): MX forward 455 -> 413 us
+    // and MX weight gradient 801 -> 718 us against 4 waves; at 16 waves its DMA offsets and
+    // accumulators spill inside the loop (827 / 1267 us).
     constexpr int NW = MXV == MX_NONE ? 16 : 8;
     gemm256_kernel<FMT, MODE, MXV, NW><<<dim3((unsigned)grid), dim3(64 * NW), 0, stream>>>(p);
     FP8Q_CHECK_LAUNCH();
