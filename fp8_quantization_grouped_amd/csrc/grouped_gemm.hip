@@ -15,11 +15,12 @@
 //     each owning a 128x32 sub-tile (16 v_mfma_f32_16x16x128_f8f6f4 per step, 64 accumulators
 //     per lane), so the other waves' matrix instructions cover one wave's LDS reads, DMA issue
 //     and waits (one wave per SIMD is bound by its own instruction issue, not by the matrix
-//     cores).  MX: 8 waves, two per SIMD, each 128x64 (32 MFMAs per step, 128 accumulators).
+//     cores).  MX with its scales by DMA: the same 16 waves; MX with byte-loaded scales: 8
+//     waves, two per SIMD, each 128x64 (32 MFMAs per step, 128 accumulators).
 //   * Operand tiles go HBM/L2 -> LDS directly with buffer_load_dwordx4 ... lds (no staging
 //     registers), double-buffered: after the barrier of step k the loads of step k+1 are
-//     issued in 32 parts of 8 rows x 128 bytes per operand (16 waves: 2 parts each; MX, 8
-//     waves: 4 parts each; all before the wave's first matrix instruction of the step), and
+//     issued in 32 parts of 8 rows x 128 bytes per operand (16 waves: 2 parts each; 8 waves:
+//     4 parts each; all before the wave's first matrix instruction of the step), and
 //     waited for only at the top of step k+1, so one barrier per step.
 //     Rows and chunks outside the operand are turned into out-of-range buffer offsets and read
 //     back as zeros.  Chunks are stored XOR-swizzled
@@ -607,6 +608,13 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
             const uint8_t* Bs = smem[cur_st][1];
             const bool kb_in = kpos + 32 * kg < cur.kb_hi;  // MX: this lane's K block exists
             const int mslot = (cur.mx_slot + (kk >> 2)) & 1, msub = 4 * (kk & 3);
+            // LDS indices of the scale of this lane's first A row (row wm*128 + lr); the masks
+            // change no value (both stay inside their arrays) but let the compiler fold the
+            // per-row offsets into the LDS instructions' immediates instead of holding one
+            // address register per row (16 waves: the difference between spilling and not)
+            const uint32_t ma_dma =
+                (uint32_t)(((mslot * 2 + 0) * GT + wm * 128 + lr) * 16 + msub + kg) & 0x3FFFu;
+            const uint32_t ma_byt = (uint32_t)(wm * 128 + lr) & 0xFFu;
             v8i_t bf[NJ];
             int sb_[NJ];
 #pragma unroll
@@ -643,11 +651,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
                 if (pend && MX && NW == 4 && i < NP) part(P, i);  // 4-wave MX: one part per row
                 int sa_ = 0;
                 if (MXV == MX_BYTES) {
-                    const int e = (int)((sscale[cur_st][0][rm] >> (8 * kg)) & 0xFFu);
+                    const int e = (int)((sscale[cur_st][0][ma_byt + 16 * i] >> (8 * kg)) & 0xFFu);
                     sa_ = kb_in ? e : 127;
                 }
                 if (MXV == MX_DMA) {
-                    const int e = (int)smx[((mslot * 2 + 0) * GT + rm) * 16 + msub + kg];
+                    const int e = (int)smx[ma_dma + 256 * i];
                     sa_ = kb_in ? e : 127;
                 }
 #pragma unroll
@@ -754,11 +762,11 @@ static fp8q_status_t launch_gemm(GemmArgs p, hipStream_t stream) {
     p.vec_store = (p.ldc % 8 == 0) && fp8q_aligned(p.c, 16);
     // Plain FP8: 16 waves (four per SIMD, 128 x 32 each; 124-128 registers).  Measured on the
     // dsv3 step, 4 / 8 / 16 waves: forward 368 / 352 / 328 us, weight gradient 606 / 589 /
-    // 498 us, data gradient 396 / 364 / 345 us.  MX: 8 waves (two per SIMD, 128 x 64 each;
-    // 256 registers, no spills with the DMA parts issued up front): MX forward 455 -> 413 us
-    // and MX weight gradient 801 -> 718 us against 4 waves; at 16 waves its DMA offsets and
-    // accumulators spill inside the loop (827 / 1267 us).
-    constexpr int NW = MXV == MX_NONE ? 16 : 8;
+    // 498 us, data gradient 396 / 364 / 345 us.  MX with scales by DMA: 16 waves as well
+    // (127 registers, no spills): MX forward 455 / 406 / 392 us at 4 / 8 / 16 waves.  MX with
+    // byte-loaded scales (the MX weight gradient): 8 waves (256 registers): 801 -> 713 us
+    // against 4 waves; at 16 waves its registers spill inside the loop (1267 us).
+    constexpr int NW = MXV == MX_BYTES ? 8 : 16;
     gemm256_kernel<FMT, MODE, MXV, NW><<<dim3((unsigned)grid), dim3(64 * NW), 0, stream>>>(p);
     FP8Q_CHECK_LAUNCH();
     return FP8Q_OK;
