@@ -348,7 +348,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): this path has no "
-              "multi-GPU mode; expert-parallel sharding is described in DESIGN.md.",
+              "multi-GPU mode (under expert parallelism each GPU runs this same path on its own "
+              "experts' token rows).",
               file=sys.stderr)
         sys.exit(2)
     import torch
