@@ -352,6 +352,27 @@ def test_gemm_fwd_expert_major_weights(fq, fmt):
     gemm_tol_check(c.float().cpu().numpy(), ref, "fwd expert-major")
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemm_fwd_rows_isolated_from_other_groups(fq, fmt):
+    """A group's outputs depend on its own rows only: the rows of the next group in its partial
+    row tiles hold NaN codes (e4m3fn 0x7F, e4m3fnuz 0x80), and groups 0 (5 rows, inside one
+    tile with 251 rows of group 1) and 2 must still match the oracle."""
+    M, K, N, E = 600, 256, 128, 3
+    off = np.array([5, 300, 600], np.int32)
+    qa, sa, qbt, sb = _fwd_operands(fmt, M, K, N, E, 77)
+    qa = qa.copy()
+    qa[5:300] = 0x7F if fmt == FN else 0x80
+    c = fq.fp8_grouped_gemm(fq.GEMM_FWD_MGROUPED, fmt, torch.from_numpy(qa).to(DEV),
+                            torch.from_numpy(sa).to(DEV), torch.from_numpy(qbt).to(DEV),
+                            torch.from_numpy(sb).to(DEV), dev_i32(off), M, N, K,
+                            ldb=E * K, b_group_stride=K)
+    got = c.float().cpu().numpy()
+    rows = np.concatenate([np.arange(0, 5), np.arange(300, 600)])
+    ref = oracle.gemm_fwd_rows(fmt, qa, sa, qbt, E * K, K, sb, off, N, K, rows)
+    assert np.all(np.isfinite(got[rows]))
+    gemm_tol_check(got[rows], ref, "fwd rows isolated")
+
+
 DGRAD_CASES = [
     # M (tokens), K (hidden, the output columns), N (intermediate, the contraction), offsets
     (1024, 256, 512, [485, 524, 774, 1024]),    # the C1 shapes and offsets
