@@ -272,6 +272,7 @@ WDUAL_CASES = [
     (3, 64, 2048, 0),    # the widest N
     (2, 130, 8, 16),     # one 8-column chunk per row
     (1, 1, 16, 0),
+    (16, 4096, 2048, 16),  # long expert groups, padded strides
 ]
 
 
