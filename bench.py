@@ -123,6 +123,7 @@ class Step:
         self.buf = dict(
             xq=e(M, K), sx=e(M, dt=f32), wqt=e(N, E * K), sw=e(E, N, dt=f32), y=e(M, N, dt=bf),
             ws_w=e(max(256, fq.fp8_quant_colwise_grouped_workspace_size(E * K, N, E))),
+            gws=e(fq.fp8_grouped_gemm_workspace_size(0, M, N, K, int(d["offsets"].numel()))),
         )
         if "wgrad" in d["ops"]:
             self.buf.update(
@@ -202,7 +203,7 @@ class Step:
                 workspace=b["ws_w"])),
             ("gemm_fwd", lambda: fq.fp8_grouped_gemm(
                 fq.GEMM_FWD_MGROUPED, fmt, b["xq"], b["sx"], b["wqt"], b["sw"], d["offsets"],
-                M, N, K, ldb=E * K, b_group_stride=K, c=b["y"])),
+                M, N, K, ldb=E * K, b_group_stride=K, c=b["y"], workspace=b["gws"])),
         ]
         # rows beyond the hot-path step (gathered dispatch quant, data gradient, MX backward):
         # timed in passes of their own after the step
@@ -220,7 +221,7 @@ class Step:
                     workspace=b["ws_dy"])),
                 ("gemm_wgrad", lambda: fq.fp8_grouped_gemm(
                     fq.GEMM_WGRAD_KGROUPED, fmt, b["xqt"], b["sxg"], b["dyqt"], b["sdyg"],
-                    d["offsets"], M, N, K, ldb=self.ldm, c=b["dw"])),
+                    d["offsets"], M, N, K, ldb=self.ldm, c=b["dw"], workspace=b["gws"])),
             ]
         if "dgrad" in d["ops"]:
             # dX[m, k] = sum_n dY[m, n] W_g[k, n]: the forward mode with W's [K, N] rows of expert
@@ -232,7 +233,8 @@ class Step:
                                                                  scales=b["swk"])),
                 ("gemm_dgrad", lambda: fq.fp8_grouped_gemm(
                     fq.GEMM_FWD_MGROUPED, fmt, b["dyq"], b["sdyr"], b["wqn"], b["swk"],
-                    d["offsets"], M, K, N, ldb=N, b_group_stride=K * N, c=b["dx"])),
+                    d["offsets"], M, K, N, ldb=N, b_group_stride=K * N, c=b["dx"],
+                    workspace=b["gws"])),
                 ("quant_weights_dual", lambda: fq.fp8_quant_weights_dual(
                     d["w"], E, fmt, q_rows=b["dwr"], s_rows=b["dwrs"], q_t=b["dwt"],
                     s_cols=b["dwts"], workspace=b["ws_dual"])),
@@ -246,7 +248,7 @@ class Step:
                 ("gemm_mx", lambda: fq.fp8_mx_grouped_gemm(
                     b["mxq"], b["mxe"], b["mxwt"], b["mxwe"], d["offsets"], M, N, K,
                     ldb=E * K, b_group_stride=K, ld_sb=E * K // 32, sb_group_stride=K // 32,
-                    c=b["ymx"])),
+                    c=b["ymx"], workspace=b["gws"])),
             ]
         if "mxwgrad" in d["ops"]:
             extra += [
@@ -256,7 +258,7 @@ class Step:
                     d["dy"], q_t=b["mxdyt"], e8m0=b["mxdye"])),
                 ("gemm_mx_wgrad", lambda: fq.fp8_mx_grouped_gemm_wgrad(
                     b["mxxt"], b["mxxe"], b["mxdyt"], b["mxdye"], d["offsets"], M, N, K,
-                    c=b["mxdw"])),
+                    c=b["mxdw"], workspace=b["gws"])),
             ]
         return seq, extra
 

@@ -22,6 +22,8 @@ E4M3FN = 1    # OCP e4m3fn: largest value 448
 FMAX = {E4M3FNUZ: 240.0, E4M3FN: 448.0}
 GEMM_FWD_MGROUPED = 0
 GEMM_WGRAD_KGROUPED = 1
+OUT_BF16 = 0
+OUT_FP32 = 1
 
 _lib = None
 
@@ -31,6 +33,9 @@ _I = ctypes.c_int
 SIGNATURES = {
     "fp8q_abi_version": (_I, []),
     "fp8q_status_string": (ctypes.c_char_p, [_I]),
+    "fp8_abi_version": (_I, []),
+    "fp8_status_string": (ctypes.c_char_p, [_I]),
+    "fp8_grouped_gemm_workspace_size": (_SZ, [_I, _I64, _I64, _I64, _I32]),
     "fp8_quant_rowwise": (_I, [_P, _I64, _I64, _I64, _I, _P, _I64, _P, _P]),
     "fp8_quant_rowwise_gather": (_I, [_P, _I64, _I64, _I64, _P, _I64, _I, _P, _I64, _P, _P]),
     "fp8_quant_colwise_grouped_workspace_size": (_SZ, [_I64, _I64, _I32]),
@@ -40,13 +45,13 @@ SIGNATURES = {
     "fp8_quant_weights_dual": (_I, [_P, _I64, _I64, _I64, _I64, _I, _P, _I64, _P, _P, _I64, _P, _P,
                                     _SZ, _P]),
     "fp8_grouped_gemm": (_I, [_I, _I, _P, _I64, _P, _P, _I64, _I64, _P, _P, _I32, _I64, _I64,
-                              _I64, _P, _I64, _P]),
+                              _I64, _P, _I64, _I, _P, _SZ, _P]),
     "fp8_mx_quant_rowwise": (_I, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P]),
     "fp8_mx_quant_colwise": (_I, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P]),
     "fp8_mx_grouped_gemm": (_I, [_P, _I64, _P, _I64, _P, _I64, _I64, _P, _I64, _I64, _P, _I32,
-                                 _I64, _I64, _I64, _P, _I64, _P]),
+                                 _I64, _I64, _I64, _P, _I64, _I, _P, _SZ, _P]),
     "fp8_mx_grouped_gemm_wgrad": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I32, _I64,
-                                       _I64, _I64, _P, _I64, _P]),
+                                       _I64, _I64, _P, _I64, _I, _P, _SZ, _P]),
 }
 
 
@@ -190,24 +195,59 @@ def fp8_quant_weights_dual(w: torch.Tensor, experts: int, fmt: int,
     return (q_rows, s_rows), (q_t, s_cols)
 
 
+def fp8_grouped_gemm_workspace_size(mode: int, M: int, N: int, K: int, groups: int) -> int:
+    return int(lib().fp8_grouped_gemm_workspace_size(mode, M, N, K, groups))
+
+
+_OUT = {torch.bfloat16: OUT_BF16, torch.float32: OUT_FP32}
+
+
+def _gemm_out(c, shape, out_dtype, dev):
+    if c is None:
+        c = torch.empty(shape, dtype=out_dtype, device=dev)
+    if c.dtype not in _OUT:
+        raise ValueError("the GEMM output must be bfloat16 or float32")
+    if c.dim() != len(shape) or tuple(c.shape) != tuple(shape) or c.stride(-1) != 1:
+        raise ValueError(f"the GEMM output must be {tuple(shape)} with unit column stride")
+    if len(shape) == 3 and c.stride(0) != shape[1] * c.stride(1):
+        raise ValueError("a weight-gradient output's group stride must be K * ldc")
+    return c
+
+
+def _gemm_ws(workspace, mode, M, N, K, groups, dev):
+    need = fp8_grouped_gemm_workspace_size(mode, M, N, K, groups)
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    return workspace
+
+
+def gemm_offsets_status(workspace: torch.Tensor):
+    """The offsets check a grouped GEMM wrote into its workspace: (status, first bad group);
+    (0, -1) for valid offsets.  Synchronises with the device to read it."""
+    w = workspace[:8].view(torch.int32).cpu()
+    return int(w[0]), int(w[1])
+
+
 def fp8_grouped_gemm(mode: int, fmt: int, a: torch.Tensor, a_scales: torch.Tensor,
                      b: torch.Tensor, b_scales: torch.Tensor, offsets: torch.Tensor, M: int,
                      N: int, K: int, ldb: int | None = None, b_group_stride: int = 0,
-                     c: torch.Tensor | None = None):
+                     c: torch.Tensor | None = None, out_dtype=torch.bfloat16,
+                     workspace: torch.Tensor | None = None):
     """Scaled FP8 grouped GEMM (see the C header for the two modes).
     Forward: a [M, lda], b holds every group's [N, K] rows at ldb / b_group_stride; returns
-    bf16 [M, N].  Weight gradient: a [K, lda >= M], b [N, ldb >= M]; returns bf16 [G, K, N]."""
+    [M, N].  Weight gradient: a [K, lda >= M], b [N, ldb >= M]; returns [G, K, N].  The output
+    is bfloat16 or float32 (out_dtype, or the dtype of a given c)."""
     _dev(a, "a")
     groups = offsets.numel()
     if ldb is None:
         ldb = b.stride(0)
-    if c is None:
-        shape = (M, N) if mode == GEMM_FWD_MGROUPED else (groups, K, N)
-        c = torch.empty(shape, dtype=torch.bfloat16, device=a.device)
-    ldc = c.stride(-2)
+    shape = (M, N) if mode == GEMM_FWD_MGROUPED else (groups, K, N)
+    c = _gemm_out(c, shape, out_dtype, a.device)
+    ws = _gemm_ws(workspace, mode, M, N, K, groups, a.device)
     st = lib().fp8_grouped_gemm(mode, fmt, _ptr(a), a.stride(0), _ptr(a_scales), _ptr(b), ldb,
                                 b_group_stride, _ptr(b_scales), _ptr(offsets), groups, M, N, K,
-                                _ptr(c), ldc, _stream(a))
+                                _ptr(c), c.stride(-2), _OUT[c.dtype], _ptr(ws), ws.numel(),
+                                _stream(a))
     _check("fp8_grouped_gemm", st)
     return c
 
@@ -248,32 +288,34 @@ def fp8_mx_quant_colwise(x: torch.Tensor, q_t: torch.Tensor | None = None,
 def fp8_mx_grouped_gemm(a: torch.Tensor, a_e8m0: torch.Tensor, b: torch.Tensor,
                         b_e8m0: torch.Tensor, offsets: torch.Tensor, M: int, N: int, K: int,
                         ldb: int, b_group_stride: int, ld_sb: int, sb_group_stride: int,
-                        c: torch.Tensor | None = None):
-    """MX grouped GEMM forward; returns bf16 [M, N]."""
+                        c: torch.Tensor | None = None, out_dtype=torch.bfloat16,
+                        workspace: torch.Tensor | None = None):
+    """MX grouped GEMM forward; returns [M, N] (bfloat16 or float32)."""
     _dev(a, "a")
     groups = offsets.numel()
-    if c is None:
-        c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    c = _gemm_out(c, (M, N), out_dtype, a.device)
+    ws = _gemm_ws(workspace, GEMM_FWD_MGROUPED, M, N, K, groups, a.device)
     st = lib().fp8_mx_grouped_gemm(_ptr(a), a.stride(0), _ptr(a_e8m0), a_e8m0.stride(0), _ptr(b),
                                    ldb, b_group_stride, _ptr(b_e8m0), ld_sb, sb_group_stride,
                                    _ptr(offsets), groups, M, N, K, _ptr(c), c.stride(0),
-                                   _stream(a))
+                                   _OUT[c.dtype], _ptr(ws), ws.numel(), _stream(a))
     _check("fp8_mx_grouped_gemm", st)
     return c
 
 
 def fp8_mx_grouped_gemm_wgrad(a: torch.Tensor, a_e8m0: torch.Tensor, b: torch.Tensor,
                               b_e8m0: torch.Tensor, offsets: torch.Tensor, M: int, N: int,
-                              K: int, c: torch.Tensor | None = None):
+                              K: int, c: torch.Tensor | None = None, out_dtype=torch.bfloat16,
+                              workspace: torch.Tensor | None = None):
     """MX weight gradient: a = XqT [K, lda >= M], b = dYqT [N, ldb >= M] with E8M0 per 32
-    tokens (fp8_mx_quant_colwise outputs).  Returns bf16 [G, K, N]."""
+    tokens (fp8_mx_quant_colwise outputs).  Returns [G, K, N] (bfloat16 or float32)."""
     _dev(a, "a")
     groups = offsets.numel()
-    if c is None:
-        c = torch.empty((groups, K, N), dtype=torch.bfloat16, device=a.device)
+    c = _gemm_out(c, (groups, K, N), out_dtype, a.device)
+    ws = _gemm_ws(workspace, GEMM_WGRAD_KGROUPED, M, N, K, groups, a.device)
     st = lib().fp8_mx_grouped_gemm_wgrad(_ptr(a), a.stride(0), _ptr(a_e8m0), a_e8m0.stride(0),
                                          _ptr(b), b.stride(0), _ptr(b_e8m0), b_e8m0.stride(0),
                                          _ptr(offsets), groups, M, N, K, _ptr(c), c.stride(-2),
-                                         _stream(a))
+                                         _OUT[c.dtype], _ptr(ws), ws.numel(), _stream(a))
     _check("fp8_mx_grouped_gemm_wgrad", st)
     return c

@@ -51,6 +51,8 @@
 // largest first) in LDS, takes an even share of the work for its XCD, and walks its tiles.
 // Offsets are clamped into [0, M] before use, so any offsets content keeps every access in
 // range.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace fp8q {
@@ -108,6 +110,7 @@ __device__ __forceinline__ void dma4(i32x4_t rsrc, uint32_t voff, uint32_t lds_b
                  : "memory", "m0");
 }
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)p);
 }
@@ -177,11 +180,13 @@ struct GemmArgs {
     const int32_t* offsets;
     int G;
     int64_t M, N, K;
-    uint16_t* c;
+    uint8_t* c;       // bf16 or fp32 elements (out_f32), row stride ldc elements
     int64_t ldc;
+    int32_t* status;  // offsets check result (two words), written by block 0
     int nt_n;         // column tiles
     int nt_k;         // wgrad: row tiles along K
-    bool vec_store;   // 16-byte aligned output octets
+    bool out_f32;     // fp32 output instead of bf16
+    bool vec_store;   // N, ldc multiples of 8 and c 16-byte aligned: whole 16-byte stores
 };
 
 constexpr int GMAX = 2048;  // groups whose schedule prefix fits in LDS
@@ -224,6 +229,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
     pref_t* s_part = reinterpret_cast<pref_t*>(&smem[1][0][0]);  // scan scratch (set-up only)
     // weight gradient: groups in schedule order (most contraction steps first)
     __shared__ unsigned short s_perm[MODE == MODE_WGRAD ? GMAX : 1];
+    __shared__ int s_bad;                                   // offsets check (block 0)
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     // NW = 4: each wave owns 128 x 128 of the tile; NW = 8: 128 x 64; NW = 16: 128 x 32
@@ -245,6 +251,25 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
         __syncthreads();
     }
     auto off_at = [&](int g) -> int { return OFF_LDS ? s_off[g] : p.offsets[g]; };
+    // Offsets check, block 0: the first group whose end lies below its start or past M, or a
+    // last end other than M, is reported in status[1] (status[0] = FP8Q_ERR_INVALID_ARG);
+    // valid offsets give {FP8Q_OK, -1}.  The kernel itself only ever uses clamped offsets, so
+    // invalid ones change results but never the memory accessed.
+    if (p.status != nullptr && blockIdx.x == 0) {
+        if (t == 0) s_bad = 0x7FFFFFFF;
+        __syncthreads();
+        for (int i = t; i < p.G; i += NT) {
+            const int64_t lo = i == 0 ? 0 : (int64_t)off_at(i - 1);
+            const int64_t hi = off_at(i);
+            if (hi < lo || hi > p.M || (i == p.G - 1 && hi != p.M)) atomicMin(&s_bad, i);
+        }
+        __syncthreads();
+        if (t == 0) {
+            const int bad = s_bad;
+            p.status[0] = bad == 0x7FFFFFFF ? (int32_t)FP8Q_OK : (int32_t)FP8Q_ERR_INVALID_ARG;
+            p.status[1] = bad == 0x7FFFFFFF ? -1 : bad;
+        }
+    }
     // group g's token rows, clamped into [0, M] so that any offsets content stays in range
     auto rows_of = [&](int g, int64_t& lo, int64_t& hi) {
         lo = g == 0 ? 0 : (int64_t)off_at(g - 1);
@@ -567,15 +592,23 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
                 scales_pending = false;
             }
             if (MODE == MODE_WGRAD && (kpos < cur.kb_lo || kpos + GK > cur.kb_hi)) {
-                // zero the activation bytes of neighbouring groups in the straddling chunks
+                // zero the bytes of other tokens (neighbouring groups, or the padding past M)
+                // in the straddling chunks of BOTH operands: such a byte may hold any code,
+                // NaN included, and 0 * NaN would reach the group's sums
                 __syncthreads();
                 const int lo = cur.kb_lo - kpos, hi = cur.kb_hi - kpos;
-                if (row_thread) {
+                // threads 0-255 take the rows of the activation tile, 256-511 those of the
+                // gradient tile (at least 8 waves: wave-uniform sides)
+                static_assert(NW >= 8, "two tile sides over 512 threads");
+                if (t < 2 * GT) {
+                    const int zr = t & (GT - 1);
+                    uint8_t* side = smem[cur_st][t >> 8];
 #pragma unroll
                     for (int ch = 0; ch < 8; ch++) {
                         const int b0 = 16 * ch;
                         if ((lo > b0 && lo < b0 + 16) || (hi > b0 && hi < b0 + 16)) {
-                            uint4* q = reinterpret_cast<uint4*>(&smem[cur_st][0][lds_off(t, ch)]);
+                            uint4* q = reinterpret_cast<uint4*>(
+                                side + (t < GT ? lds_off(zr, ch) : lds_offB(zr, ch)));
                             uint4 w = *q;
                             w.x &= keep_mask4(lo, hi, b0);
                             w.y &= keep_mask4(lo, hi, b0 + 4);
@@ -687,8 +720,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
         }
 
         // Epilogue: lane holds rows row_lo + wm*128 + 16i + lane%16 and, per column-block pair
-        // j', the 8 consecutive columns n0 + wn*128 + 32j' + 8*(lane/16) + 0..7 (blocks 2j' and
-        // 2j'+1 give 4 each).  Dequantize with the reciprocal scales and store 8 bf16 at once.
+        // j', the 8 consecutive columns n0 + wn*WNC + 32j' + 8*(lane/16) + 0..7 (blocks 2j' and
+        // 2j'+1 give 4 each).  Dequantize with the reciprocal scales and store 8 outputs at once.
         const float* s_rows = reinterpret_cast<const float*>(sscale[cur.par][0]);
         const float* s_cols = reinterpret_cast<const float*>(sscale[cur.par][1]);
         const bool scaled = !MX && cur.nk > 0;  // an empty contraction stores zeros
@@ -696,34 +729,87 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
 #pragma unroll
         for (int i = 0; i < 8; i++)
             rs[i] = scaled ? __builtin_amdgcn_rcpf(s_rows[wm * 128 + i * 16 + lr]) : 1.0f;
+        const int64_t crow0 = MODE == MODE_FWD ? (int64_t)cur.row_lo : (int64_t)cur.g * p.K + cur.row_lo;
+        const int trows = cur.row_hi - cur.row_lo;
+        // Stores go through a buffer resource over the tile's output rows; a row past the
+        // tile's last one or a column past N gets an out-of-range lane offset and its store is
+        // dropped (the range check covers the lane offset only, never the scalar offset, so the
+        // whole address is in the lane offset).  Branch-free: every wave issues the same store
+        // instructions.
+        const uint32_t esz = p.out_f32 ? 4u : 2u;
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(
+            p.c + crow0 * p.ldc * (int64_t)esz, (uint32_t)trows * (uint32_t)p.ldc * esz);
+        const uint32_t row16 = 16u * (uint32_t)p.ldc * esz;  // bytes of 16 output rows
+        auto epilogue = [&](auto f32, auto vec) {
+            constexpr bool F32 = decltype(f32)::value, VEC = decltype(vec)::value;
+            constexpr uint32_t ES = F32 ? 4u : 2u;
 #pragma unroll
-        for (int jp = 0; jp < NJ / 2; jp++) {
-            const int n = cur.n0 + wn * WNC + 32 * jp + 8 * lq;
-            float cs[8];
+            for (int jp = 0; jp < NJ / 2; jp++) {
+                const int nl = wn * WNC + 32 * jp + 8 * lq;
+                const int n = cur.n0 + nl;
+                const uint32_t lane_off =
+                    ((uint32_t)(wm * 128 + lr) * (uint32_t)p.ldc + (uint32_t)n) * ES;
+                float cs[8];
 #pragma unroll
-            for (int e = 0; e < 8; e++)
-                cs[e] = scaled ? __builtin_amdgcn_rcpf(s_cols[wn * WNC + 32 * jp + 8 * lq + e]) : 1.0f;
+                for (int e = 0; e < 8; e++)
+                    cs[e] = scaled ? __builtin_amdgcn_rcpf(s_cols[nl + e]) : 1.0f;
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const int m = cur.row_lo + wm * 128 + i * 16 + lr;
-                if (m >= cur.row_hi) continue;
-                uint16_t* crow =
-                    p.c + (MODE == MODE_FWD ? (int64_t)m : (int64_t)cur.g * p.K + m) * p.ldc;
-                const v4f_t a0 = acc[i][2 * jp], a1 = acc[i][2 * jp + 1];
-                const float r_ = rs[i];
-                const uint32_t w0 = pack_bf16x2(a0[0] * r_ * cs[0], a0[1] * r_ * cs[1]);
-                const uint32_t w1 = pack_bf16x2(a0[2] * r_ * cs[2], a0[3] * r_ * cs[3]);
-                const uint32_t w2 = pack_bf16x2(a1[0] * r_ * cs[4], a1[1] * r_ * cs[5]);
-                const uint32_t w3 = pack_bf16x2(a1[2] * r_ * cs[6], a1[3] * r_ * cs[7]);
-                if (p.vec_store && n + 7 < p.N) {
-                    *reinterpret_cast<uint4*>(crow + n) = make_uint4(w0, w1, w2, w3);
-                } else {
-                    const uint32_t w[4] = {w0, w1, w2, w3};
+                for (int i = 0; i < 8; i++) {
+                    const bool row_ok = wm * 128 + i * 16 + lr < trows;
+                    const uint32_t roff = lane_off + (uint32_t)i * row16;
+                    const v4f_t a0 = acc[i][2 * jp], a1 = acc[i][2 * jp + 1];
+                    const float r_ = rs[i];
+                    float v[8];
 #pragma unroll
-                    for (int e = 0; e < 8; e++)
-                        if (n + e < p.N) crow[n + e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+                    for (int e = 0; e < 4; e++) {
+                        v[e] = a0[e] * r_ * cs[e];
+                        v[4 + e] = a1[e] * r_ * cs[4 + e];
+                    }
+                    if (VEC) {
+                        // N is a multiple of 8: a lane's 8 columns are all inside or all past N
+                        const uint32_t off = row_ok && n < p.N ? roff : OOB;
+                        if (F32) {
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                i32x4_t{(int)__float_as_uint(v[0]), (int)__float_as_uint(v[1]),
+                                        (int)__float_as_uint(v[2]), (int)__float_as_uint(v[3])},
+                                rc, off, 0, 0);
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                i32x4_t{(int)__float_as_uint(v[4]), (int)__float_as_uint(v[5]),
+                                        (int)__float_as_uint(v[6]), (int)__float_as_uint(v[7])},
+                                rc, off + 16u, 0, 0);
+                        } else {
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                i32x4_t{(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3]),
+                                        (int)pack_bf16x2(v[4], v[5]), (int)pack_bf16x2(v[6], v[7])},
+                                rc, off, 0, 0);
+                        }
+                    } else {
+                        // any N, ldc and (element-aligned) c: one store per element
+#pragma unroll
+                        for (int e = 0; e < 8; e++) {
+                            const uint32_t off =
+                                row_ok && n + e < p.N ? roff + (uint32_t)e * ES : OOB;
+                            if (F32)
+                                __builtin_amdgcn_raw_buffer_store_b32((int)__float_as_uint(v[e]), rc,
+                                                                      off, 0, 0);
+                            else
+                                __builtin_amdgcn_raw_buffer_store_b16(
+                                    (short)(pack_bf16x2(v[e], 0.0f) & 0xFFFFu), rc, off, 0, 0);
+                        }
+                    }
                 }
             }
+        };
+        if (p.vec_store) {
+            if (p.out_f32)
+                epilogue(std::true_type{}, std::true_type{});
+            else
+                epilogue(std::false_type{}, std::true_type{});
+        } else {
+            if (p.out_f32)
+                epilogue(std::true_type{}, std::false_type{});
+            else
+                epilogue(std::false_type{}, std::false_type{});
         }
         stage0 = (stage0 + (cur.nk & 1)) & 1;
         have = have_next;
@@ -756,13 +842,14 @@ static fp8q_status_t launch_gemm(GemmArgs p, hipStream_t stream) {
     const int64_t max_tiles = MODE == MODE_FWD ? ((p.M + GT - 1) / GT + p.G) * p.nt_n
                                                : (int64_t)p.G * p.nt_k * p.nt_n;
     if (max_tiles >= 0x7FFFFFFFLL) return FP8Q_ERR_UNSUPPORTED;
-    // Upper bound of tiles (forward: each group may add one partial row tile).
-    const int64_t tiles = MODE == MODE_FWD ? ((p.M + GT - 1) / GT + p.G) * p.nt_n
-                                           : (int64_t)p.G * p.nt_k * p.nt_n;
     int64_t grid = num_cus();
-    if (tiles < grid) grid = tiles;
+    if (max_tiles < grid) grid = max_tiles;
     if (grid < 1) grid = 1;
-    p.vec_store = (p.ldc % 8 == 0) && fp8q_aligned(p.c, 16);
+    // whole 16-byte output stores through a 32-bit buffer range over a tile's 256 rows
+    const int64_t esz = p.out_f32 ? 4 : 2;
+    if ((int64_t)GT * p.ldc * esz >= 0x7FFFFFFFLL) return FP8Q_ERR_UNSUPPORTED;
+    if (!fp8q_aligned(p.c, (uintptr_t)esz)) return FP8Q_ERR_INVALID_ARG;
+    p.vec_store = p.N % 8 == 0 && p.ldc % 8 == 0 && fp8q_aligned(p.c, 16);
     // Plain FP8: 16 waves (four per SIMD, 128 x 32 each; 124-128 registers).  Measured on the
     // dsv3 step, 4 / 8 / 16 waves: forward 368 / 352 / 328 us, weight gradient 606 / 589 /
     // 498 us, data gradient 396 / 364 / 345 us.  MX with scales by DMA: 16 waves as well
@@ -780,21 +867,45 @@ static inline bool offsets_fit(int64_t lda, int64_t ldb) {
     return (int64_t)GT * lda < 0x7FFFFFFFLL && (int64_t)GT * ldb < 0x7FFFFFFFLL;
 }
 
+// Workspace of every grouped GEMM: the two status words of the offsets check, padded.
+constexpr size_t kGemmWorkspace = 256;
+
+// Output type, workspace and the fields they set; FP8Q_OK or the status to return.
+static fp8q_status_t gemm_common(GemmArgs& p, fp8q_out_t out_dtype, void* workspace,
+                                 size_t workspace_bytes) {
+    if (out_dtype != FP8Q_OUT_BF16 && out_dtype != FP8Q_OUT_FP32) return FP8Q_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < kGemmWorkspace) return FP8Q_ERR_WORKSPACE;
+    if (!fp8q_aligned(workspace, 4)) return FP8Q_ERR_INVALID_ARG;
+    p.out_f32 = out_dtype == FP8Q_OUT_FP32;
+    p.status = reinterpret_cast<int32_t*>(workspace);
+    return FP8Q_OK;
+}
+
 }  // namespace fp8q
+
+extern "C" size_t fp8_grouped_gemm_workspace_size(fp8q_gemm_mode_t mode, int64_t M, int64_t N,
+                                                  int64_t K, int32_t groups) {
+    (void)mode; (void)M; (void)N; (void)K; (void)groups;
+    return fp8q::kGemmWorkspace;
+}
 
 extern "C" fp8q_status_t fp8_grouped_gemm(fp8q_gemm_mode_t mode, fp8q_format_t fmt,
                                           const uint8_t* a, int64_t lda, const float* a_scales,
                                           const uint8_t* b, int64_t ldb, int64_t b_group_stride,
                                           const float* b_scales, const int32_t* offsets,
                                           int32_t groups, int64_t M, int64_t N, int64_t K,
-                                          uint16_t* c, int64_t ldc, hipStream_t stream) {
+                                          void* c, int64_t ldc, fp8q_out_t out_dtype,
+                                          void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream) {
     using namespace fp8q;
     if (!fp8q_fmt_ok(fmt) || groups < 1 || M < 0 || N < 0 || K < 0 || ldc < N || !offsets)
         return FP8Q_ERR_INVALID_ARG;
     GemmArgs p{};
+    const fp8q_status_t cs = gemm_common(p, out_dtype, workspace, workspace_bytes);
+    if (cs != FP8Q_OK) return cs;
     p.a = a; p.lda = lda; p.a_scales = a_scales; p.b = b; p.ldb = ldb; p.bgs = b_group_stride;
     p.b_scales = b_scales; p.offsets = offsets; p.G = groups; p.M = M; p.N = N; p.K = K;
-    p.c = c; p.ldc = ldc;
+    p.c = reinterpret_cast<uint8_t*>(c); p.ldc = ldc;
     if (mode == FP8Q_GEMM_FWD_MGROUPED) {
         if (lda < K || ldb < K || b_group_stride < 0) return FP8Q_ERR_INVALID_ARG;
         if (M == 0 || N == 0) return FP8Q_OK;
@@ -823,22 +934,27 @@ extern "C" fp8q_status_t fp8_mx_grouped_gemm_wgrad(const uint8_t* a, int64_t lda
                                                    const uint8_t* b, int64_t ldb,
                                                    const uint8_t* b_e8m0, int64_t ld_sb,
                                                    const int32_t* offsets, int32_t groups,
-                                                   int64_t M, int64_t N, int64_t K, uint16_t* c,
-                                                   int64_t ldc, hipStream_t stream) {
+                                                   int64_t M, int64_t N, int64_t K, void* c,
+                                                   int64_t ldc, fp8q_out_t out_dtype,
+                                                   void* workspace, size_t workspace_bytes,
+                                                   hipStream_t stream) {
     using namespace fp8q;
     if (groups < 1 || M < 0 || N < 0 || K < 0 || ldc < N || !offsets || lda < M || ldb < M ||
         ld_sa < M / 32 || ld_sb < M / 32)
         return FP8Q_ERR_INVALID_ARG;
     if (M % 32) return FP8Q_ERR_INVALID_ARG;
+    GemmArgs p{};
+    const fp8q_status_t cs = gemm_common(p, out_dtype, workspace, workspace_bytes);
+    if (cs != FP8Q_OK) return cs;
     if (K == 0 || N == 0) return FP8Q_OK;
     if (!a_e8m0 || !b_e8m0 || !c || (M > 0 && (!a || !b))) return FP8Q_ERR_INVALID_ARG;
     if (lda % 16 || ldb % 16 || !fp8q_aligned(a, 16) || !fp8q_aligned(b, 16) ||
         !offsets_fit(lda, ldb) || !offsets_fit(ld_sa, ld_sb))
         return FP8Q_ERR_UNSUPPORTED;
-    GemmArgs p{};
     p.a = a; p.lda = lda; p.a_e8 = a_e8m0; p.ld_sa = ld_sa; p.b = b; p.ldb = ldb;
     p.bgs = 0; p.b_e8 = b_e8m0; p.ld_sb = ld_sb; p.sbgs = 0;
-    p.offsets = offsets; p.G = groups; p.M = M; p.N = N; p.K = K; p.c = c; p.ldc = ldc;
+    p.offsets = offsets; p.G = groups; p.M = M; p.N = N; p.K = K;
+    p.c = reinterpret_cast<uint8_t*>(c); p.ldc = ldc;
     // per-step byte loads of the scales: a tile's first 32-token block need not be 16-aligned
     return launch_gemm<FP8Q_E4M3FN, MODE_WGRAD, MX_BYTES>(p, stream);
 }
@@ -848,22 +964,26 @@ extern "C" fp8q_status_t fp8_mx_grouped_gemm(const uint8_t* a, int64_t lda, cons
                                              int64_t b_group_stride, const uint8_t* b_e8m0,
                                              int64_t ld_sb, int64_t sb_group_stride,
                                              const int32_t* offsets, int32_t groups, int64_t M,
-                                             int64_t N, int64_t K, uint16_t* c, int64_t ldc,
-                                             hipStream_t stream) {
+                                             int64_t N, int64_t K, void* c, int64_t ldc,
+                                             fp8q_out_t out_dtype, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream) {
     using namespace fp8q;
     if (groups < 1 || M < 0 || N < 0 || K < 0 || ldc < N || !offsets || lda < K || ldb < K ||
         b_group_stride < 0 || sb_group_stride < 0 || ld_sa < K / 32 || ld_sb < K / 32)
         return FP8Q_ERR_INVALID_ARG;
     if (K % 32) return FP8Q_ERR_INVALID_ARG;
+    GemmArgs p{};
+    const fp8q_status_t cs = gemm_common(p, out_dtype, workspace, workspace_bytes);
+    if (cs != FP8Q_OK) return cs;
     if (M == 0 || N == 0) return FP8Q_OK;
     if (!a || !b || !a_e8m0 || !b_e8m0 || !c) return FP8Q_ERR_INVALID_ARG;
     if (lda % 16 || ldb % 16 || b_group_stride % 16 || !fp8q_aligned(a, 16) ||
         !fp8q_aligned(b, 16) || !offsets_fit(lda, ldb) || !offsets_fit(ld_sa, ld_sb))
         return FP8Q_ERR_UNSUPPORTED;
-    GemmArgs p{};
     p.a = a; p.lda = lda; p.a_e8 = a_e8m0; p.ld_sa = ld_sa; p.b = b; p.ldb = ldb;
     p.bgs = b_group_stride; p.b_e8 = b_e8m0; p.ld_sb = ld_sb; p.sbgs = sb_group_stride;
-    p.offsets = offsets; p.G = groups; p.M = M; p.N = N; p.K = K; p.c = c; p.ldc = ldc;
+    p.offsets = offsets; p.G = groups; p.M = M; p.N = N; p.K = K;
+    p.c = reinterpret_cast<uint8_t*>(c); p.ldc = ldc;
     const bool dma = ld_sa % 16 == 0 && ld_sb % 16 == 0 && sb_group_stride % 16 == 0 &&
                      fp8q_aligned(a_e8m0, 16) && fp8q_aligned(b_e8m0, 16);
     if (dma) return launch_gemm<FP8Q_E4M3FN, MODE_FWD, MX_DMA>(p, stream);

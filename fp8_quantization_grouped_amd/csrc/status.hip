@@ -13,3 +13,7 @@ extern "C" const char* fp8q_status_string(fp8q_status_t status) {
     }
     return "unknown status";
 }
+
+extern "C" int fp8_abi_version(void) { return fp8q_abi_version(); }
+
+extern "C" const char* fp8_status_string(fp8q_status_t status) { return fp8q_status_string(status); }

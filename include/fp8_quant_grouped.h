@@ -28,7 +28,10 @@
  *   - Matrices are row-major with an explicit leading dimension (elements between rows).
  *   - Offsets: int32[groups], the cumulative END row of each group: group g covers rows
  *     [offsets[g-1], offsets[g]) with offsets[-1] = 0.  Non-decreasing, offsets[groups-1] equals
- *     the row count, empty groups allowed.  Violations are undefined behaviour (not checked).
+ *     the row count, empty groups allowed.  The quantizers do not check this (violations give
+ *     unspecified results); the grouped GEMMs check it on the device and report the result in
+ *     their workspace (see fp8_grouped_gemm).  No offsets content makes a kernel access memory
+ *     outside its operands.
  *   - Inputs must be finite.  Behaviour on NaN/Inf inputs is unspecified.
  *   - Host-checkable violations (null pointer, negative size, leading dimension too small,
  *     unknown format, workspace too small, a size beyond a kernel's limit) return a status
@@ -51,7 +54,7 @@ extern "C" {
 
 typedef struct ihipStream_t* hipStream_t;
 
-#define FP8Q_ABI_VERSION 1
+#define FP8Q_ABI_VERSION 2
 
 /* FP8 element encoding.  e4m3fnuz: bias 8, largest value 240, single zero, 0x80 is NaN
  * ("La correttezza del formato viene prima del tuning").  e4m3fn: OCP e4m3, bias 7, largest
@@ -68,9 +71,15 @@ typedef enum {
 
 typedef enum { FP8Q_GEMM_FWD_MGROUPED = 0, FP8Q_GEMM_WGRAD_KGROUPED = 1 } fp8q_gemm_mode_t;
 
-/* ABI version (FP8Q_ABI_VERSION) and a static text for a status code. */
+/* Element type of a grouped GEMM's output: bf16 (round to nearest even) or fp32. */
+typedef enum { FP8Q_OUT_BF16 = 0, FP8Q_OUT_FP32 = 1 } fp8q_out_t;
+
+/* ABI version (FP8Q_ABI_VERSION) and a static text for a status code; the fp8_* names are the
+ * same functions. */
 int fp8q_abi_version(void);
 const char* fp8q_status_string(fp8q_status_t status);
+int fp8_abi_version(void);
+const char* fp8_status_string(fp8q_status_t status);
 
 /* Rowwise quantization of activations (ai-radar.it, introduction and "Il guadagno vero e' nel
  * movimento dei dati": one scale per token row, chain absmax -> scale -> clamp -> cast, fused
@@ -143,8 +152,8 @@ fp8q_status_t fp8_quant_colwise_grouped(const uint16_t* x, int64_t rows, int64_t
  *   q_t      u8 [N][ld_qt], ld_qt >= experts*K      s_cols fp32 [experts][N]
  *   workspace >= fp8_quant_weights_dual_workspace_size(experts, K, N) bytes, any content.
  * Limits (FP8Q_ERR_UNSUPPORTED, nothing launched): N <= 2048, N, ld_w and ld_qr multiples of 8,
- * w 16-byte and q_rows 8-byte aligned, experts * ceil(K/64) < 2^31.  experts == 0, K == 0 or
- * N == 0 is a no-op. */
+ * w 16-byte and q_rows 8-byte aligned, experts * K < 2^31 and experts * ceil(K/128) < 2^31
+ * (128-row blocks along K).  experts == 0, K == 0 or N == 0 is a no-op. */
 size_t fp8_quant_weights_dual_workspace_size(int64_t experts, int64_t K, int64_t N);
 fp8q_status_t fp8_quant_weights_dual(const uint16_t* w, int64_t experts, int64_t K, int64_t N,
                                      int64_t ld_w, fp8q_format_t fmt, uint8_t* q_rows,
@@ -152,10 +161,17 @@ fp8q_status_t fp8_quant_weights_dual(const uint16_t* w, int64_t experts, int64_t
                                      float* s_cols, void* workspace, size_t workspace_bytes,
                                      hipStream_t stream);
 
+/* Workspace bytes of the grouped GEMMs (fp8_grouped_gemm, fp8_mx_grouped_gemm and
+ * fp8_mx_grouped_gemm_wgrad) for the given problem.  The workspace receives the offsets check
+ * (below); its content before the call does not matter. */
+size_t fp8_grouped_gemm_workspace_size(fp8q_gemm_mode_t mode, int64_t M, int64_t N, int64_t K,
+                                       int32_t groups);
+
 /* Scaled FP8 grouped GEMM with fp32 accumulation on FP8 MFMA and dequantization fused into
- * the epilogue; bf16 output, rounded to nearest even (latestnews.news third paragraph: grouped
- * GEMM for MoE on ROCm; fosswire.org "What Primus adds for MoE training on MI355X": FP8 grouped
- * GEMM for the expert FFNs).  fmt is the encoding of both operands.
+ * the epilogue (latestnews.news third paragraph: grouped GEMM for MoE on ROCm; fosswire.org
+ * "What Primus adds for MoE training on MI355X": FP8 grouped GEMM for the expert FFNs;
+ * ai-radar.it introduction: rowwise activation scales, colwise expert-weight scales, the
+ * offset tensor routing token rows to experts).  fmt is the encoding of both operands.
  *
  * mode FP8Q_GEMM_FWD_MGROUPED (forward, groups along M):
  *   a         Xq  u8 [M][lda], lda >= K               a_scales fp32 [M]
@@ -163,29 +179,46 @@ fp8q_status_t fp8_quant_weights_dual(const uint16_t* w, int64_t experts, int64_t
  *             K bytes each (K-contiguous) ldb >= K    b_scales fp32 [groups][N]
  *             (weights quantized by fp8_quant_colwise_grouped into [N, E*K]: ldb = E*K,
  *             b_group_stride = K; weights stored [E,N,K]: ldb = K, b_group_stride = N*K)
- *   c         bf16 [M][ldc], ldc >= N
- *   c[m,n] = bf16( (sum_k dec(a[m,k]) * dec(b_g[n,k])) * (1/a_scales[m]) * (1/b_scales[g,n]) )
+ *   c         [M][ldc] of out_dtype, ldc >= N
+ *   c[m,n] = (sum_k dec(a[m,k]) * dec(b_g[n,k])) * (1/a_scales[m]) * (1/b_scales[g,n])
  *   for m in group g.
  * mode FP8Q_GEMM_WGRAD_KGROUPED (weight gradient, groups along the contraction dimension):
  *   a         XqT u8 [K][lda], lda >= M (column-major quantized activations)
  *   a_scales  fp32 [groups][K]
  *   b         dYqT u8 [N][ldb], ldb >= M              b_scales fp32 [groups][N]
  *   b_group_stride must be 0
- *   c         bf16 [groups][K][ldc], ldc >= N, group stride K*ldc
- *   c[g,k,n] = bf16( (sum_{m in g} dec(a[k,m]) * dec(b[n,m])) / (a_scales[g,k]*b_scales[g,n]) )
- *   An empty group writes zeros.
- * Accumulation is fp32 on the matrix cores; the result is within 1e-3 + 1e-2*|exact| of the
- * exactly accumulated value for the sizes this library targets.  Element bits of c are not
- * specified beyond that bound.
+ *   c         [groups][K][ldc] of out_dtype, ldc >= N, group stride K*ldc
+ *   c[g,k,n] = (sum_{m in g} dec(a[k,m]) * dec(b[n,m])) * (1/a_scales[g,k]) * (1/b_scales[g,n])
+ *   An empty group writes zeros.  Only the bytes of tokens [0, M) are used: the padding of
+ *   the token dimension (columns M..ld-1) and the bytes of other groups may hold any codes.
+ *
+ * Offsets check: the kernel writes two int32 words at the start of the workspace:
+ *   {FP8Q_OK, -1} for valid offsets, or {FP8Q_ERR_INVALID_ARG, g} where g is the first group
+ *   whose end lies below its start or beyond M, or the last group when offsets[groups-1] != M.
+ *   The words are written on the stream (read them after it, no host synchronisation is done);
+ *   a call with an empty output launches nothing and writes nothing.  With invalid offsets the
+ *   kernel still only reads and writes inside the operands (offsets are clamped into [0, M]),
+ *   but the results are unspecified.
+ *
+ * Accuracy: the matrix cores sum each 8 consecutive contraction products in fixed point whose
+ * last bit is 2^-13 of 2^E, E the largest exponent sum (exponent of a plus exponent of b) in
+ * the 8, each product truncated toward zero, and add those partial sums into an fp32
+ * accumulator (measured on gfx950).  So |c - exact| <= sum over the 8-product groups of
+ * (nonzero products) * 2^(E-13) / (a_scale * b_scale), plus fp32 accumulation rounding (about
+ * 2^-23 of the summed magnitudes), plus the final rounding to out_dtype.  Element bits of c are
+ * not specified beyond that bound.
+ *
  * Kernel limits (FP8Q_ERR_UNSUPPORTED, nothing launched): forward needs K, lda, ldb and
  * b_group_stride multiples of 16; weight gradient needs lda and ldb multiples of 16 (pad the
- * token dimension; the padding is never read); a and b 16-byte aligned; groups <= 2048;
- * M, N, K < 2^31 and 256 * lda, 256 * ldb < 2^31. */
+ * token dimension); a and b 16-byte aligned; groups <= 2048; M, N, K < 2^31 and 256 * lda,
+ * 256 * ldb < 2^31.  Other errors: FP8Q_ERR_WORKSPACE for a null or too small workspace,
+ * FP8Q_ERR_INVALID_ARG for an unknown out_dtype or a workspace not 4-byte aligned. */
 fp8q_status_t fp8_grouped_gemm(fp8q_gemm_mode_t mode, fp8q_format_t fmt, const uint8_t* a,
                                int64_t lda, const float* a_scales, const uint8_t* b,
                                int64_t ldb, int64_t b_group_stride, const float* b_scales,
                                const int32_t* offsets, int32_t groups, int64_t M, int64_t N,
-                               int64_t K, uint16_t* c, int64_t ldc, hipStream_t stream);
+                               int64_t K, void* c, int64_t ldc, fp8q_out_t out_dtype,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* MXFP8 quantization along rows (OCP MX v1.0; the pages only name MXFP8 kernels for MI355X in
  * "What Primus adds for MoE training on MI355X"): blocks of 32 consecutive elements of a row
@@ -210,18 +243,22 @@ fp8q_status_t fp8_mx_quant_colwise(const uint16_t* x, int64_t rows, int64_t cols
                                    hipStream_t stream);
 
 /* MXFP8 grouped GEMM, forward (groups along M), on gfx950's block-scaled FP8 MFMA:
- *   c[m,n] = bf16( sum_kb 2^(ea[m,kb] + eb_g[n,kb]) * sum_{k in kb} dec(a[m,k]) * dec(b_g[n,k]) )
+ *   c[m,n] = sum_kb 2^(ea[m,kb] + eb_g[n,kb]) * sum_{k in kb} dec(a[m,k]) * dec(b_g[n,k])
  * with ea = a_e8m0[m*ld_sa + kb] - 127, eb_g = b_e8m0[g*sb_group_stride + n*ld_sb + kb] - 127,
  * b_g = b + g*b_group_stride (rows n at stride ldb), K % 32 == 0, e4m3fn elements, fp32
  * accumulation.  Weights from fp8_mx_quant_colwise on [E*K, N]: ldb = E*K,
  * b_group_stride = K, ld_sb = E*K/32, sb_group_stride = K/32.
- * Limits as for the forward FP8 GEMM, plus 256 * ld_sa, 256 * ld_sb < 2^31. */
+ * c is [M][ldc] of out_dtype; workspace, offsets check and accuracy as for fp8_grouped_gemm
+ * (each 8-product group lies inside one 32-element scale block; the E8M0 factors scale the
+ * partial sums exactly).  Limits as for the forward FP8 GEMM, plus 256 * ld_sa,
+ * 256 * ld_sb < 2^31. */
 fp8q_status_t fp8_mx_grouped_gemm(const uint8_t* a, int64_t lda, const uint8_t* a_e8m0,
                                   int64_t ld_sa, const uint8_t* b, int64_t ldb,
                                   int64_t b_group_stride, const uint8_t* b_e8m0, int64_t ld_sb,
                                   int64_t sb_group_stride, const int32_t* offsets,
-                                  int32_t groups, int64_t M, int64_t N, int64_t K, uint16_t* c,
-                                  int64_t ldc, hipStream_t stream);
+                                  int32_t groups, int64_t M, int64_t N, int64_t K, void* c,
+                                  int64_t ldc, fp8q_out_t out_dtype, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
 
 /* MXFP8 grouped GEMM, weight gradient (groups along the token dimension, which is the
  * contraction) -- the MX backward (fosswire.org "AMD Primus adds FP8/MXFP8 kernels ...",
@@ -230,20 +267,22 @@ fp8q_status_t fp8_mx_grouped_gemm(const uint8_t* a, int64_t lda, const uint8_t* 
  * [M, K] and dY [M, N] from fp8_mx_quant_colwise: scale blocks are 32 consecutive tokens counted
  * from token 0, so a block may straddle a group boundary; it keeps its one scale and each group
  * sums only its own tokens:
- *   c[(g*K + k)*ldc + n] = bf16( sum_{m in g} dec(a[k,m]) 2^(ea[k, m/32]) dec(b[n,m]) 2^(eb[n, m/32]) )
+ *   c[(g*K + k)*ldc + n] = sum_{m in g} dec(a[k,m]) 2^(ea[k, m/32]) dec(b[n,m]) 2^(eb[n, m/32])
  * with ea = a_e8m0[k*ld_sa + m/32] - 127, eb = b_e8m0[n*ld_sb + m/32] - 127; empty groups write
  * zeros.
  *   a       XqT u8 [K][lda], lda >= M;  a_e8m0 [K][ld_sa], ld_sa >= M/32
  *   b       dYqT u8 [N][ldb], ldb >= M; b_e8m0 [N][ld_sb], ld_sb >= M/32
  *   offsets int32 [groups] device (as for the FP8 weight gradient); M % 32 == 0
- *   c       bf16 [groups][K][ldc], ldc >= N
- * Limits as for the FP8 weight-gradient GEMM, plus 256 * ld_sa, 256 * ld_sb < 2^31. */
+ *   c       [groups][K][ldc] of out_dtype, ldc >= N
+ * Workspace, offsets check and accuracy as for fp8_grouped_gemm.  Limits as for the FP8
+ * weight-gradient GEMM, plus 256 * ld_sa, 256 * ld_sb < 2^31. */
 fp8q_status_t fp8_mx_grouped_gemm_wgrad(const uint8_t* a, int64_t lda, const uint8_t* a_e8m0,
                                         int64_t ld_sa, const uint8_t* b, int64_t ldb,
                                         const uint8_t* b_e8m0, int64_t ld_sb,
                                         const int32_t* offsets, int32_t groups, int64_t M,
-                                        int64_t N, int64_t K, uint16_t* c, int64_t ldc,
-                                        hipStream_t stream);
+                                        int64_t N, int64_t K, void* c, int64_t ldc,
+                                        fp8q_out_t out_dtype, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -236,3 +236,113 @@ def mx_gemm_wgrad_rows(xt, xe8, dyt, de8, offsets, N, g_idx, k_idx):
                                   dyt.shape[1], _p(de8), de8.shape[1], _p(off), off.shape[0], N,
                                   _p(gi), _p(ki), gi.shape[0], _p(out))
     return out
+
+# ----------------------------------------------------------------------------- whole-matrix GEMMs
+# The same definitions as gemm_fwd_rows / gemm_wgrad_rows, for every output at once, with a
+# library matmul as the summation step (numpy float64, multithreaded BLAS) so that full-size
+# outputs take seconds.  Exactness: every decoded FP8 value times 2^9 (e4m3fn) or 2^10
+# (e4m3fnuz) is an integer below 2^18 in magnitude, so every product of two such integers is
+# an integer below 2^36 and every partial sum of up to 2^17 of them an integer below 2^53:
+# float64 adds them without rounding, in whatever order the matmul takes.  The sums are thus
+# the exact ones the C oracle forms, and the results equal its output bit for bit.
+
+_INT_SCALE = {FNUZ: 10, FN: 9}  # log2 of the factor that makes every decoded value an integer
+
+
+def decode_table(fmt: int) -> np.ndarray:
+    """float64 [256]: the C oracle's decode of every byte (NaN for the NaN codes)."""
+    return np.array([decode(fmt, b) for b in range(256)], np.float64)
+
+
+def _int_operand(fmt: int, q: np.ndarray) -> np.ndarray:
+    lut = decode_table(fmt) * 2.0 ** _INT_SCALE[fmt]
+    return lut[np.asarray(q, np.uint8)]
+
+
+def gemm_fwd_full(fmt, a, sa, b, ldb, b_gs, sb, offsets, N, K):
+    """Every row of the forward grouped GEMM: float64 [M, N], the exact sum of
+    dec(a[m,k]) dec(b[g*b_gs + n*ldb + k]) over k, divided by sa[m]*sb[g,n] in float64 (the value
+    gemm_fwd_rows returns).  a: uint8 [M, >= K]; b: flat uint8 buffer; rows of no group give 0."""
+    a = np.asarray(a, np.uint8)
+    M = a.shape[0]
+    bflat = np.ascontiguousarray(b, np.uint8).reshape(-1)
+    off = np.asarray(offsets, np.int64)
+    sa = np.asarray(sa, np.float32).astype(np.float64)
+    sb = np.asarray(sb, np.float32).astype(np.float64).reshape(off.size, N)
+    out = np.zeros((M, N), np.float64)
+    unit = 2.0 ** (-2 * _INT_SCALE[fmt])
+    lo = 0
+    for g, hi in enumerate(off):
+        hi = int(hi)
+        if hi > lo:
+            idx = g * b_gs + np.arange(N)[:, None] * ldb + np.arange(K)[None, :]
+            bg = _int_operand(fmt, bflat[idx])                 # [N, K]
+            ag = _int_operand(fmt, a[lo:hi, :K])               # [rows, K]
+            acc = (ag @ bg.T) * unit                            # exact sums
+            out[lo:hi] = acc / (sa[lo:hi, None] * sb[g][None, :])
+        lo = max(lo, hi)
+    return out
+
+
+def gemm_wgrad_group(fmt, xt, sx, dyt, sdy, offsets, g):
+    """dW_g of the K-grouped weight gradient: float64 [K, N], the exact sum over the group's
+    tokens m of dec(xt[k,m]) dec(dyt[n,m]), divided by sx[g,k]*sdy[g,n] in float64 (the value
+    gemm_wgrad_rows returns).  xt: uint8 [K, >= M]; dyt: uint8 [N, >= M]."""
+    off = np.asarray(offsets, np.int64)
+    lo = 0 if g == 0 else int(off[g - 1])
+    hi = int(off[g])
+    K, N = xt.shape[0], dyt.shape[0]
+    if hi <= lo:
+        return np.zeros((K, N), np.float64)
+    unit = 2.0 ** (-2 * _INT_SCALE[fmt])
+    acc = (_int_operand(fmt, xt[:, lo:hi]) @ _int_operand(fmt, dyt[:, lo:hi]).T) * unit
+    sxg = np.asarray(sx, np.float32).astype(np.float64).reshape(off.size, K)[g]
+    sdg = np.asarray(sdy, np.float32).astype(np.float64).reshape(off.size, N)[g]
+    return acc / (sxg[:, None] * sdg[None, :])
+
+
+def _mx_operand(q: np.ndarray, e8: np.ndarray) -> np.ndarray:
+    """float64 values dec(q) * 2^(e8 - 127), one E8M0 byte per 32 consecutive elements of a row
+    (exact: a 4-bit significand times a power of two)."""
+    lut = decode_table(FN)
+    v = lut[np.asarray(q, np.uint8)]
+    sc = np.exp2(np.repeat(np.asarray(e8, np.float64), 32, axis=1)[:, :v.shape[1]] - 127.0)
+    return v * sc
+
+
+def mx_gemm_fwd_full(a, ae8, b, ldb, b_gs, be8, ld_sb, bs_gs, offsets, N, K):
+    """Every row of the MX grouped GEMM forward: float64 [M, N] of
+    sum_kb 2^(ea+eb) sum_{k in kb} dec(a) dec(b) -- the products exact, their sum rounded in
+    float64 (relative error below K * 2^-53, far inside any GEMM tolerance)."""
+    a = np.asarray(a, np.uint8)
+    M = a.shape[0]
+    off = np.asarray(offsets, np.int64)
+    bflat = np.ascontiguousarray(b, np.uint8).reshape(-1)
+    beflat = np.ascontiguousarray(be8, np.uint8).reshape(-1)
+    nb = K // 32
+    out = np.zeros((M, N), np.float64)
+    lo = 0
+    for g, hi in enumerate(off):
+        hi = int(hi)
+        if hi > lo:
+            qb = bflat[g * b_gs + np.arange(N)[:, None] * ldb + np.arange(K)[None, :]]
+            eb = beflat[g * bs_gs + np.arange(N)[:, None] * ld_sb + np.arange(nb)[None, :]]
+            out[lo:hi] = _mx_operand(a[lo:hi, :K], np.asarray(ae8)[lo:hi, :nb]) @ \
+                _mx_operand(qb, eb).T
+        lo = max(lo, hi)
+    return out
+
+
+def mx_gemm_wgrad_group(xt, xe8, dyt, de8, offsets, g):
+    """dW_g of the MX weight gradient: float64 [K, N] of the sum over the group's tokens of
+    dec(xt[k,m]) 2^(xe8[k,m/32]-127) dec(dyt[n,m]) 2^(de8[n,m/32]-127), summed in float64."""
+    off = np.asarray(offsets, np.int64)
+    lo = 0 if g == 0 else int(off[g - 1])
+    hi = int(off[g])
+    K, N = xt.shape[0], dyt.shape[0]
+    if hi <= lo:
+        return np.zeros((K, N), np.float64)
+    b0, b1 = lo // 32, -(-hi // 32)
+    xa = _mx_operand(xt[:, b0 * 32:b1 * 32], np.asarray(xe8)[:, b0:b1])
+    da = _mx_operand(dyt[:, b0 * 32:b1 * 32], np.asarray(de8)[:, b0:b1])
+    return xa[:, lo - b0 * 32:hi - b0 * 32] @ da[:, lo - b0 * 32:hi - b0 * 32].T

@@ -32,11 +32,16 @@
  *     e4m3fn keeps the sign of zero (0x80 for -0 and negative underflow);
  *   - offsets are int32 cumulative group END indices, offsets[G-1] == rows, empty groups allowed;
  *   - the colwise output is the column-major copy of the whole 2-D input, q_t[c * ld + r];
- *   - grouped GEMM output: bf16, round to nearest even, of the exact sum scaled by 1/(s_a*s_b).
+ *   - grouped GEMM output: the exact sum divided by s_a*s_b (the caller's output type, bf16 or
+ *     fp32, is a rounding of it).
  *
  * Precision: the quantization chain is evaluated in IEEE fp32 (the precision in which the
- * GPU takes the same integer decisions); GEMM sums are accumulated in fp64, where every sum of
- * fp8 x fp8 products up to K = 2^20 terms is exact.
+ * GPU takes the same integer decisions).  GEMM sums are accumulated in fp64: every fp8 x fp8
+ * product is a multiple of 2^-18 (e4m3fn) or 2^-20 (e4m3fnuz) below 2^17.7 in magnitude, so
+ * every partial sum of up to 2^17 terms is exactly representable and the sum is exact (all
+ * contractions here are far shorter).  The exact sum is then divided by the fp64 product of
+ * the two fp32 scales and returned unrounded; it is the value the matrix cores' fp32
+ * accumulation approximates.
  *
  * Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off -fno-fast-math -fPIC -shared -lm
  */

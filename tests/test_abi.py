@@ -30,8 +30,9 @@ def test_header_declares_the_hot_path():
                  "fp8_grouped_gemm",
                  "fp8_mx_quant_rowwise", "fp8_mx_quant_colwise", "fp8_mx_grouped_gemm",
                  "fp8_mx_grouped_gemm_wgrad",
-                 "fp8_quant_colwise_grouped_workspace_size", "fp8q_status_string",
-                 "fp8q_abi_version"):
+                 "fp8_quant_colwise_grouped_workspace_size", "fp8_grouped_gemm_workspace_size",
+                 "fp8q_status_string", "fp8q_abi_version", "fp8_status_string",
+                 "fp8_abi_version"):
         assert must in names
     text = open(HEADER).read()
     assert "torch" not in re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -55,12 +56,20 @@ def test_binding_covers_every_symbol():
 
 
 def test_host_only_calls(lib):
-    lib.fp8q_abi_version.restype = ctypes.c_int
-    assert lib.fp8q_abi_version() == 1
-    lib.fp8q_status_string.restype = ctypes.c_char_p
-    lib.fp8q_status_string.argtypes = [ctypes.c_int]
-    assert lib.fp8q_status_string(0) == b"ok"
-    assert lib.fp8q_status_string(3) == b"workspace too small"
+    for ver, txt in (("fp8q_abi_version", "fp8q_status_string"),
+                     ("fp8_abi_version", "fp8_status_string")):
+        getattr(lib, ver).restype = ctypes.c_int
+        assert getattr(lib, ver)() == 2
+        f = getattr(lib, txt)
+        f.restype = ctypes.c_char_p
+        f.argtypes = [ctypes.c_int]
+        assert f(0) == b"ok"
+        assert f(3) == b"workspace too small"
+        assert f(99) == b"unknown status"
+    ws = lib.fp8_grouped_gemm_workspace_size
+    ws.restype = ctypes.c_size_t
+    ws.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
+    assert ws(0, 16384, 2048, 7168, 32) >= 8 and ws(1, 16384, 2048, 7168, 32) >= 8
     f = lib.fp8_quant_colwise_grouped_workspace_size
     f.restype = ctypes.c_size_t
     f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
@@ -89,20 +98,38 @@ def test_argument_errors_are_caught_on_the_host(lib):
     assert gq(dummy, 0, 8, 8, None, 0, 1, dummy, 8, dummy, None) == 0    # empty: no-op
     g = lib.fp8_grouped_gemm
     g.restype = I
-    g.argtypes = [I, I, P, I64, P, P, I64, I64, P, P, ctypes.c_int32, I64, I64, I64, P, I64, P]
-    assert g(5, 1, dummy, 16, dummy, dummy, 16, 0, dummy, dummy, 1, 4, 4, 16, dummy, 4, None) == 1
-    assert g(0, 1, dummy, 16, dummy, dummy, 16, 0, dummy, dummy, 0, 4, 4, 16, dummy, 4, None) == 1
-    assert g(1, 1, dummy, 16, dummy, dummy, 16, 16, dummy, dummy, 1, 4, 4, 16, dummy, 4,
-             None) == 1  # wgrad needs b_group_stride == 0
+    SZ = ctypes.c_size_t
+    g.argtypes = [I, I, P, I64, P, P, I64, I64, P, P, ctypes.c_int32, I64, I64, I64, P, I64, I, P,
+                  SZ, P]
+    ws = ctypes.c_void_p(256)  # 4-byte aligned, never dereferenced either
+    assert g(5, 1, dummy, 16, dummy, dummy, 16, 0, dummy, dummy, 1, 4, 4, 16, dummy, 4, 0, ws, 256,
+             None) == 1  # unknown mode
+    assert g(0, 1, dummy, 16, dummy, dummy, 16, 0, dummy, dummy, 0, 4, 4, 16, dummy, 4, 0, ws, 256,
+             None) == 1  # no groups
+    assert g(1, 1, dummy, 16, dummy, dummy, 16, 16, dummy, dummy, 1, 4, 4, 16, dummy, 4, 0, ws,
+             256, None) == 1  # wgrad needs b_group_stride == 0
+    assert g(0, 1, dummy, 16, dummy, dummy, 16, 0, dummy, dummy, 1, 4, 4, 16, dummy, 4, 2, ws, 256,
+             None) == 1  # unknown output type
+    assert g(0, 1, dummy, 16, dummy, dummy, 16, 0, dummy, dummy, 1, 4, 4, 16, dummy, 4, 0, None,
+             256, None) == 3  # no workspace
+    assert g(0, 1, dummy, 16, dummy, dummy, 16, 0, dummy, dummy, 1, 4, 4, 16, dummy, 4, 0, ws, 8,
+             None) == 3  # workspace too small
+    assert g(0, 1, dummy, 16, dummy, dummy, 16, 0, dummy, dummy, 1, 0, 4, 16, dummy, 4, 1, ws, 256,
+             None) == 0  # M == 0: no-op
+    assert g(0, 1, dummy, 16, dummy, dummy, 16, 0, dummy, dummy, 1, 4, 4, 8, dummy, 4, 0, ws, 256,
+             None) == 2  # K not a multiple of 16
     mw = lib.fp8_mx_grouped_gemm_wgrad
     mw.restype = I
-    mw.argtypes = [P, I64, P, I64, P, I64, P, I64, P, ctypes.c_int32, I64, I64, I64, P, I64, P]
-    assert mw(dummy, 48, dummy, 2, dummy, 48, dummy, 2, dummy, 1, 48, 16, 16, dummy, 16,
-              None) == 1  # M not a multiple of 32
-    assert mw(dummy, 64, dummy, 1, dummy, 64, dummy, 2, dummy, 1, 64, 16, 16, dummy, 16,
-              None) == 1  # scale rows shorter than M/32
-    assert mw(dummy, 64, dummy, 2, dummy, 64, dummy, 2, dummy, 1, 64, 0, 16, dummy, 16,
-              None) == 0  # N == 0: no-op
+    mw.argtypes = [P, I64, P, I64, P, I64, P, I64, P, ctypes.c_int32, I64, I64, I64, P, I64, I, P,
+                   SZ, P]
+    assert mw(dummy, 48, dummy, 2, dummy, 48, dummy, 2, dummy, 1, 48, 16, 16, dummy, 16, 0, ws,
+              256, None) == 1  # M not a multiple of 32
+    assert mw(dummy, 64, dummy, 1, dummy, 64, dummy, 2, dummy, 1, 64, 16, 16, dummy, 16, 0, ws,
+              256, None) == 1  # scale rows shorter than M/32
+    assert mw(dummy, 64, dummy, 2, dummy, 64, dummy, 2, dummy, 1, 64, 0, 16, dummy, 16, 0, ws,
+              256, None) == 0  # N == 0: no-op
+    assert mw(dummy, 64, dummy, 2, dummy, 64, dummy, 2, dummy, 1, 64, 16, 16, dummy, 16, 0, ws,
+              100, None) == 3  # workspace too small
 
 
 def test_device_code_has_no_generic_memory_instructions():

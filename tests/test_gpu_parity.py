@@ -574,5 +574,127 @@ def test_invalid_arguments_return_status(fq):
     off = dev_i32([4])
     assert L.fp8_quant_colwise_grouped(p(x), 4, 8, 8, p(off), 1, 1, p(q), 4, p(s), p(q), 4,
                                        None) == 3  # workspace too small
+    ws = torch.zeros((256,), dtype=torch.uint8, device=DEV)
     assert L.fp8_grouped_gemm(0, 1, p(q), 8, p(s), p(q), 8, 0, p(s), p(off), 1, 4, 4, 8, p(x),
-                              4, None) == 2  # K not a multiple of 16
+                              4, 0, p(ws), 256, None) == 2  # K not a multiple of 16
+
+
+# ----------------------------------------------------------------------------- GEMM contract
+
+def _wgrad_case(fmt, M, K, N, off, seed):
+    x = workloads.make_matrix(seed, M, K)
+    dy = workloads.make_matrix(seed + 1, M, N)
+    xt, sx = oracle.quant_colwise_grouped(x, off, fmt)
+    dyt, sdy = oracle.quant_colwise_grouped(dy, off, fmt)
+    return xt, sx, dyt, sdy
+
+
+def test_gemm_wgrad_ignores_padding_and_other_groups_codes(fq):
+    """Weight gradient in e4m3fn with M % 16 != 0: the token padding of both operands holds NaN
+    codes (0x7F, 0xFF), as torch.empty memory may, and in a second call group 0's gradient bytes
+    are NaN codes too.  Every group's dW must still match the oracle (second call: group 1,
+    whose first contraction chunk holds group 0's last tokens)."""
+    M, K, N = 777, 200, 72
+    off = np.array([300, 777], np.int32)
+    xt, sx, dyt, sdy = _wgrad_case(FN, M, K, N, off, 1500)
+    ldp = -(-M // 16) * 16
+    a = np.full((K, ldp), 0xFF, np.uint8)
+    a[:, :M] = xt
+    b = np.full((N, ldp), 0x7F, np.uint8)
+    b[:, :M] = dyt
+    gi = np.repeat(np.arange(2, dtype=np.int32), K)
+    ki = np.tile(np.arange(K, dtype=np.int64), 2)
+    ref = oracle.gemm_wgrad_rows(FN, xt, sx, dyt, sdy, off, N, K, gi, ki).reshape(2, K, N)
+    run = lambda bb: fq.fp8_grouped_gemm(
+        fq.GEMM_WGRAD_KGROUPED, FN, torch.from_numpy(a).to(DEV), torch.from_numpy(sx).to(DEV),
+        torch.from_numpy(bb).to(DEV), torch.from_numpy(sdy).to(DEV), dev_i32(off), M, N, K,
+        ldb=ldp).float().cpu().numpy()
+    got = run(b)
+    assert np.all(np.isfinite(got))
+    gemm_tol_check(got, ref, "wgrad, NaN codes in the padding")
+    b2 = b.copy()
+    b2[:, :300] = 0x7F
+    got2 = run(b2)
+    assert np.all(np.isfinite(got2[1]))
+    gemm_tol_check(got2[1], ref[1], "wgrad, NaN codes in the previous group")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemm_fp32_output(fq, fmt):
+    """out_dtype fp32: forward and weight gradient write fp32 that matches the oracle, and the
+    bf16 output is exactly that fp32 value rounded to nearest even."""
+    M, K, N, E = 515, 512, 130, 5
+    off = np.array([128, 128, 256, 300, 515], np.int32)
+    qa, sa, qbt, sb = _fwd_operands(fmt, M, K, N, E, 815)
+    args = (fq.GEMM_FWD_MGROUPED, fmt, torch.from_numpy(qa).to(DEV), torch.from_numpy(sa).to(DEV),
+            torch.from_numpy(qbt).to(DEV), torch.from_numpy(sb).to(DEV), dev_i32(off), M, N, K)
+    c32 = fq.fp8_grouped_gemm(*args, ldb=E * K, b_group_stride=K, out_dtype=torch.float32)
+    c16 = fq.fp8_grouped_gemm(*args, ldb=E * K, b_group_stride=K)
+    assert c32.dtype == torch.float32 and c16.dtype == torch.bfloat16
+    ref = oracle.gemm_fwd_rows(fmt, qa, sa, qbt, E * K, K, sb, off, N, K, np.arange(M))
+    gemm_tol_check(c32.cpu().numpy(), ref, "fwd fp32 out")
+    assert torch.equal(c32.to(torch.bfloat16), c16)
+    Mw, Kw, Nw = 1000, 160, 96
+    offw = np.array([100, 100, 357, 358, 1000], np.int32)
+    xt, sx, dyt, sdy = _wgrad_case(fmt, Mw, Kw, Nw, offw, 1600)
+    ldp = -(-Mw // 16) * 16
+    pad = lambda v: np.pad(v, ((0, 0), (0, ldp - Mw)))
+    wargs = (fq.GEMM_WGRAD_KGROUPED, fmt, torch.from_numpy(pad(xt)).to(DEV),
+             torch.from_numpy(sx).to(DEV), torch.from_numpy(pad(dyt)).to(DEV),
+             torch.from_numpy(sdy).to(DEV), dev_i32(offw), Mw, Nw, Kw)
+    w32 = fq.fp8_grouped_gemm(*wargs, ldb=ldp, out_dtype=torch.float32)
+    w16 = fq.fp8_grouped_gemm(*wargs, ldb=ldp)
+    G = offw.size
+    gi = np.repeat(np.arange(G, dtype=np.int32), Kw)
+    ki = np.tile(np.arange(Kw, dtype=np.int64), G)
+    refw = oracle.gemm_wgrad_rows(fmt, xt, sx, dyt, sdy, offw, Nw, Kw, gi, ki).reshape(G, Kw, Nw)
+    gemm_tol_check(w32.cpu().numpy(), refw, "wgrad fp32 out")
+    assert torch.equal(w32.to(torch.bfloat16), w16)
+
+
+def test_gemm_offsets_check_in_workspace(fq):
+    """The GEMM reports its offsets check in the workspace: valid offsets give (0, -1); a
+    decreasing end or a last end other than M names the first offending group.  With such
+    offsets the kernel only uses clamped rows, so the call itself stays in range."""
+    M, K, N, E = 300, 128, 64, 3
+    qa, sa, qbt, sb = _fwd_operands(FN, M, K, N, E, 915)
+    ws = torch.full((fq.fp8_grouped_gemm_workspace_size(0, M, N, K, E),), 0xAB,
+                    dtype=torch.uint8, device=DEV)
+
+    def status(offs):
+        fq.fp8_grouped_gemm(fq.GEMM_FWD_MGROUPED, FN, torch.from_numpy(qa).to(DEV),
+                            torch.from_numpy(sa).to(DEV), torch.from_numpy(qbt).to(DEV),
+                            torch.from_numpy(sb).to(DEV), dev_i32(offs), M, N, K, ldb=E * K,
+                            b_group_stride=K, workspace=ws)
+        return fq.gemm_offsets_status(ws)
+
+    assert status([100, 200, 300]) == (0, -1)
+    assert status([0, 0, 300]) == (0, -1)
+    assert status([100, 50, 300]) == (1, 1)
+    assert status([100, 200, 250]) == (1, 2)
+    assert status([-5, 200, 300]) == (1, 0)
+    assert status([100, 400, 300]) == (1, 1)
+
+
+def test_gemm_fwd_stale_lds_rows_never_reach_stored_rows(fq):
+    """More tiles than blocks: every block of the last XCD's range first runs a full row tile of
+    group 0, whose rows are all NaN codes (e4m3fn 0x7F), then a partial tile of a small group
+    whose DMA skips the rows past the group's end (those LDS rows keep group 0's NaN bytes).
+    The small groups' rows must be finite and match the oracle."""
+    K, N = 128, 256
+    small = [5, 17, 40, 1, 200, 33, 64, 129, 255, 7, 90, 3, 16, 250, 77, 100, 2, 60, 31, 180]
+    sizes = [256 * 300] + small
+    off = np.cumsum(sizes).astype(np.int32)
+    M, E = int(off[-1]), len(sizes)
+    qa, sa, qbt, sb = _fwd_operands(FN, M, K, N, E, 1015)
+    qa = qa.copy()
+    qa[:sizes[0]] = 0x7F
+    c = fq.fp8_grouped_gemm(fq.GEMM_FWD_MGROUPED, FN, torch.from_numpy(qa).to(DEV),
+                            torch.from_numpy(sa).to(DEV), torch.from_numpy(qbt).to(DEV),
+                            torch.from_numpy(sb).to(DEV), dev_i32(off), M, N, K, ldb=E * K,
+                            b_group_stride=K)
+    rows = np.arange(sizes[0], M)
+    got = c[sizes[0]:].float().cpu().numpy()
+    ref = oracle.gemm_fwd_rows(FN, qa, sa, qbt, E * K, K, sb, off, N, K, rows)
+    assert np.all(np.isfinite(got))
+    gemm_tol_check(got, ref, "fwd after NaN tiles")

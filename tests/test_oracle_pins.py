@@ -506,3 +506,115 @@ def test_mx_wgrad_split_inside_a_block_is_additive():
              for g in (1, 2, 3)]
     assert np.allclose(parts[0] + parts[1] + parts[2], merged, rtol=1e-12, atol=0)
     assert not np.array_equal(parts[0], merged)
+
+
+# ----------------------------------------------------------------------------- whole-matrix GEMMs
+
+@pytest.mark.parametrize("fmt", FMT)
+def test_gemm_fwd_full_exact_integer_sums(fmt):
+    """gemm_fwd_full (library matmul as the summation step): every row equals the exact int64
+    sum (torch's decode tables) scaled by the float64 scale product, and the row-by-row C
+    oracle bit for bit; an empty group and rows of no group give zeros."""
+    M, K, N, E = 120, 176, 40, 4
+    off = np.array([33, 33, 100, 120], np.int32)
+    qa, sa, qbt, sb = _quantized_operands(fmt, M, K, N, E, 31, off)
+    full = oracle.gemm_fwd_full(fmt, qa, sa, qbt, E * K, K, sb, off, N, K)
+    rows = oracle.gemm_fwd_rows(fmt, qa, sa, qbt, E * K, K, sb, off, N, K, np.arange(M))
+    assert np.array_equal(full, rows)
+    ia = pinlib.int_repr(fmt, qa)
+    ib = pinlib.int_repr(fmt, qbt)
+    start = 0
+    for g, end in enumerate(off):
+        if end > start:
+            exact = ia[start:end] @ ib[:, g * K:(g + 1) * K].T
+            want = np.ldexp(exact.astype(np.float64), 2 * pinlib.QUANTUM_LOG2[fmt]) / (
+                sa[start:end, None].astype(np.float64) * sb[g][None, :].astype(np.float64))
+            assert np.array_equal(full[start:end], want)
+        start = end
+
+
+@pytest.mark.parametrize("fmt", FMT)
+def test_gemm_fwd_full_extreme_magnitudes_stay_exact(fmt):
+    """Every operand byte at the format's largest magnitude with alternating signs over a long
+    contraction (K = 16384): the partial sums reach K * FMAX^2 in the integer-scaled domain and
+    must still be exact (the integer closed form), which a float32 or low-precision sum fails."""
+    M, K, N = 4, 16384, 3
+    top = 0x7F if fmt == FNUZ else 0x7E
+    qa = np.full((M, K), top, np.uint8)
+    qa[:, 1::2] |= 0x80
+    qa[1] = top                      # row 1: all positive, sum K * FMAX^2
+    qb = np.full((N, K), top, np.uint8)
+    qb[2, :K // 2] = 0x01            # the smallest subnormal in half the terms
+    ones = np.ones(M, np.float32)
+    full = oracle.gemm_fwd_full(fmt, qa, ones, qb, K, 0, np.ones(N, np.float32),
+                                np.array([M], np.int32), N, K)
+    ia = pinlib.int_repr(fmt, qa)
+    ib = pinlib.int_repr(fmt, qb)
+    want = np.ldexp((ia @ ib.T).astype(np.float64), 2 * pinlib.QUANTUM_LOG2[fmt])
+    assert np.array_equal(full, want)
+    assert full[1, 0] == K * pinlib.FMAX[fmt] ** 2
+
+
+@pytest.mark.parametrize("fmt", FMT)
+def test_gemm_wgrad_group_matches_rows_and_integer_sums(fmt):
+    M, K, N = 300, 40, 24
+    off = np.array([0, 77, 77, 250, 300], np.int32)
+    x = workloads.make_matrix(71, M, K)
+    dy = workloads.make_matrix(72, M, N)
+    xt, sx = oracle.quant_colwise_grouped(x, off, fmt)
+    dyt, sdy = oracle.quant_colwise_grouped(dy, off, fmt)
+    ix = pinlib.int_repr(fmt, xt)
+    idy = pinlib.int_repr(fmt, dyt)
+    start = 0
+    for g, end in enumerate(off):
+        got = oracle.gemm_wgrad_group(fmt, xt, sx, dyt, sdy, off, g)
+        rows = oracle.gemm_wgrad_rows(fmt, xt, sx, dyt, sdy, off, N, K,
+                                      np.full(K, g, np.int32), np.arange(K, dtype=np.int64))
+        assert np.array_equal(got, rows)
+        exact = ix[:, start:end] @ idy[:, start:end].T
+        want = np.ldexp(exact.astype(np.float64), 2 * pinlib.QUANTUM_LOG2[fmt]) / (
+            sx[g][:, None].astype(np.float64) * sdy[g][None, :].astype(np.float64))
+        assert np.array_equal(got, want)
+        if end == start:
+            assert np.all(got == 0)
+        start = end
+
+
+def test_mx_gemm_fwd_full_matches_exact_block_sums():
+    """MX forward for every row: within 2^-50 relative of the exact rational block sums (the
+    C oracle's per-row function, separately pinned by them, as the comparison)."""
+    M, K, N, E = 64, 256, 24, 3
+    off = np.array([20, 20, 64], np.int32)
+    x = workloads.make_matrix(81, M, K, 1.0, 0.01)
+    w = workloads.make_matrix(82, E * K, N, 0.02)
+    qa, ea = oracle.mx_quant_rowwise(x)
+    qbt, eb = oracle.mx_quant_colwise(w)
+    full = oracle.mx_gemm_fwd_full(qa, ea, qbt, E * K, K, eb, E * K // 32, K // 32, off, N, K)
+    rows = oracle.mx_gemm_fwd_rows(qa, ea, qbt, E * K, K, eb, E * K // 32, K // 32, off, N, K,
+                                   np.arange(M))
+    assert np.allclose(full, rows, rtol=2.0 ** -45, atol=0)
+    ia = pinlib.int_repr(FN, qa)
+    ib = pinlib.int_repr(FN, qbt)
+    for m, n in [(0, 0), (19, 23), (20, 5), (63, 11)]:
+        g = 0 if m < 20 else 2
+        tot = Fraction(0)
+        for kb in range(K // 32):
+            s = int(np.dot(ia[m, kb * 32:(kb + 1) * 32], ib[n, g * K + kb * 32:g * K + (kb + 1) * 32]))
+            e = int(ea[m, kb]) - 127 + int(eb[n, g * K // 32 + kb]) - 127 - 18
+            tot += Fraction(s) * (Fraction(2) ** e)
+        assert abs(Fraction(full[m, n]) - tot) <= abs(tot) * Fraction(1, 2 ** 45)
+
+
+def test_mx_wgrad_group_matches_rows():
+    """MX weight gradient per group (blocks straddling group edges keep their scale) equals the
+    separately pinned per-row oracle to float64 rounding, empty groups give zeros."""
+    M, K, N = 224, 24, 20
+    off = np.array([0, 45, 45, 130, 224], np.int32)
+    xt, xe, dyt, de = _mx_wgrad_operands(M, K, N, 91)
+    for g in range(off.size):
+        got = oracle.mx_gemm_wgrad_group(xt, xe, dyt, de, off, g)
+        rows = oracle.mx_gemm_wgrad_rows(xt, xe, dyt, de, off, N, np.full(K, g, np.int32),
+                                         np.arange(K, dtype=np.int64))
+        assert np.allclose(got, rows, rtol=2.0 ** -45, atol=0)
+        if g in (0, 2):
+            assert np.all(got == 0)
