@@ -3,7 +3,8 @@
 TEST INFRASTRUCTURE ONLY: imported by the test suite, by ``__graft_entry__.smoke()`` and by the
 CPU-baseline leg of ``bench.py``, never by the GPU library or its Python binding.  The
 arithmetic lives in ``fp8_oracle.c`` (plain C, fp32 quantization chain, exact fp64 GEMM sums);
-this module only builds it with gcc and marshals numpy arrays through ctypes.
+this module builds it with gcc and marshals numpy arrays through ctypes, and adds whole-matrix
+GEMMs (below) that use a float64 library matmul as their summation step.
 
 Every function here has a pin in ``tests/test_oracle_pins.py`` except where its docstring says
 otherwise.
@@ -79,6 +80,8 @@ def _load():
                                           P]
     lib.or_num_threads.restype = ctypes.c_int
     lib.or_num_threads.argtypes = []
+    lib.or_set_num_threads.restype = None
+    lib.or_set_num_threads.argtypes = [I]
     _lib = lib
     return lib
 
@@ -93,6 +96,11 @@ def _c(a, dtype):
 
 def num_threads() -> int:
     return int(_load().or_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads for the following oracle calls."""
+    _load().or_set_num_threads(int(n))
 
 
 def fmax(fmt: int) -> float:

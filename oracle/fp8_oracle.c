@@ -378,10 +378,13 @@ void or_mx_gemm_wgrad_rows(const uint8_t* xt, int64_t ldx, const uint8_t* xe8, i
     }
 }
 
-/* Threads OpenMP will use (reported next to CPU timings). */
+/* Threads OpenMP will use (reported next to CPU timings), and a way to change it (the CPU
+ * baseline is timed at one thread and at all threads). */
 #ifdef _OPENMP
 #include <omp.h>
 int or_num_threads(void) { return omp_get_max_threads(); }
+void or_set_num_threads(int n) { if (n > 0) omp_set_num_threads(n); }
 #else
 int or_num_threads(void) { return 1; }
+void or_set_num_threads(int n) { (void)n; }
 #endif

@@ -121,12 +121,14 @@ class StrictBarCounter:
         cls.rows.append((what, int(beyond), int(total), float(worst_excess)))
 
 
-def check_gemm(got, ref, what, explain):
+def check_gemm(got, ref, what, explain, strict=False):
     """The GEMM parity bar: every element within 1e-3 + 1e-2*|ref| of the exact oracle value,
     or -- where the matrix cores' accumulation (the model above) moves a cancelling output past
-    that -- within the model's own bound: |got - model| <= ACC_REL * magnitude + output rounding.
-    explain(flat_indices) returns (model_value, magnitude) arrays in the output's units for those
-    elements.  The count of elements beyond the strict bar is recorded and reported."""
+    that -- within the model's own bound: |got - model| <= ACC_REL * magnitude + output rounding,
+    at most 1e-3 of the elements (16 for small outputs).  With strict=True no element may exceed
+    the strict bar.  explain(flat_indices) returns (model_value, magnitude) arrays in the
+    output's units for those elements.  The count of elements beyond the strict bar is
+    recorded and reported at the end of the session."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
@@ -138,6 +140,7 @@ def check_gemm(got, ref, what, explain):
     StrictBarCounter.add(what, beyond.size, err.size, max(worst, 0.0))
     if beyond.size == 0:
         return
+    assert not strict, f"{what}: {beyond.size} elements beyond the strict bar (worst {worst:.3g})"
     assert beyond.size <= max(16, 1e-3 * err.size), (
         f"{what}: {beyond.size} of {err.size} elements beyond the strict bar")
     mval, mmag = explain(beyond)
@@ -151,3 +154,121 @@ def check_gemm(got, ref, what, explain):
         f"{what}: element {beyond[i]} beyond the strict bar (gpu {g[i]:.7g}, exact "
         f"{ref.flat[beyond[i]]:.7g}) and {dev[i]:.3g} from the matrix-core model value "
         f"{mval[i]:.7g} (allowed {allow[i]:.3g})")
+
+
+# ----------------------------------------------------------------------------- explainers
+# Each returns explain(flat_indices) -> (model value, magnitude), in the GEMM's output units
+# (divided by the two dequantization scales), for check_gemm.
+
+def explain_fwd(fmt, qa, sa, b_flat, ldb, b_gs, sb, offsets, N, K, rows=None):
+    """Forward grouped GEMM; the checked output holds the rows `rows` (default: all) x N."""
+    qa = np.asarray(qa, np.uint8)
+    bflat = np.ascontiguousarray(b_flat, np.uint8).reshape(-1)
+    off = np.asarray(offsets, np.int64)
+    rows = np.arange(qa.shape[0]) if rows is None else np.asarray(rows)
+    sa = np.asarray(sa, np.float64)
+    sb = np.asarray(sb, np.float64).reshape(off.size, N)
+
+    def explain(flat):
+        vals, mags = [], []
+        for f in np.asarray(flat):
+            m, n = int(rows[f // N]), int(f % N)
+            g = int(np.searchsorted(off, m, side="right"))
+            b = bflat[g * b_gs + n * ldb:g * b_gs + n * ldb + K]
+            v, mag = model_dot(fn_bytes(fmt, qa[m, :K]), fn_bytes(fmt, b))
+            d = sa[m] * sb[g, n]
+            vals.append(v / d)
+            mags.append(mag / d)
+        return np.array(vals), np.array(mags)
+    return explain
+
+
+def explain_wgrad(fmt, xt, sx, dyt, sdy, offsets, N, K, pairs=None):
+    """Weight gradient; the checked output holds the (group, k) rows `pairs` (default: every
+    group x every k, in order) x N.  The contraction's 8-groups are absolute multiples of 8
+    tokens; another group's tokens contribute nothing."""
+    xt = np.asarray(xt, np.uint8)
+    dyt = np.asarray(dyt, np.uint8)
+    off = np.asarray(offsets, np.int64)
+    G = off.size
+    sx = np.asarray(sx, np.float64).reshape(G, K)
+    sdy = np.asarray(sdy, np.float64).reshape(G, N)
+    if pairs is None:
+        pairs = [(g, k) for g in range(G) for k in range(K)]
+
+    def explain(flat):
+        vals, mags = [], []
+        for f in np.asarray(flat):
+            g, k = pairs[f // N]
+            n = int(f % N)
+            lo = 0 if g == 0 else int(off[g - 1])
+            hi = int(off[g])
+            ks = lo - lo % GROUP
+            a = np.zeros(hi - ks, np.uint8)
+            b = np.zeros(hi - ks, np.uint8)
+            a[lo - ks:] = fn_bytes(fmt, xt[k, lo:hi])
+            b[lo - ks:] = fn_bytes(fmt, dyt[n, lo:hi])
+            v, mag = model_dot(a, b, k0=ks)
+            d = sx[g, k] * sdy[g, n]
+            vals.append(v / d)
+            mags.append(mag / d)
+        return np.array(vals), np.array(mags)
+    return explain
+
+
+def explain_mx_fwd(qa, ea, b_flat, ldb, b_gs, eb_flat, ld_sb, bs_gs, offsets, N, K, rows=None):
+    qa = np.asarray(qa, np.uint8)
+    ea = np.asarray(ea, np.uint8)
+    bflat = np.ascontiguousarray(b_flat, np.uint8).reshape(-1)
+    ebflat = np.ascontiguousarray(eb_flat, np.uint8).reshape(-1)
+    off = np.asarray(offsets, np.int64)
+    rows = np.arange(qa.shape[0]) if rows is None else np.asarray(rows)
+    nb = K // 32
+
+    def explain(flat):
+        vals, mags = [], []
+        for f in np.asarray(flat):
+            m, n = int(rows[f // N]), int(f % N)
+            g = int(np.searchsorted(off, m, side="right"))
+            b = bflat[g * b_gs + n * ldb:g * b_gs + n * ldb + K]
+            e_b = ebflat[g * bs_gs + n * ld_sb:g * bs_gs + n * ld_sb + nb].astype(np.float64)
+            fa = np.exp2(np.repeat(ea[m, :nb].astype(np.float64) - 127, 32))
+            fb = np.exp2(np.repeat(e_b - 127, 32))
+            v, mag = model_dot(qa[m, :K], b, sa=fa, sb=fb)
+            vals.append(v)
+            mags.append(mag)
+        return np.array(vals), np.array(mags)
+    return explain
+
+
+def explain_mx_wgrad(xt, xe, dyt, de, offsets, N, K, pairs=None):
+    """MX weight gradient: scale blocks are absolute 32-token blocks (a straddling block keeps
+    its scale), 8-groups absolute multiples of 8 tokens."""
+    xt = np.asarray(xt, np.uint8)
+    dyt = np.asarray(dyt, np.uint8)
+    xe = np.asarray(xe, np.float64)
+    de = np.asarray(de, np.float64)
+    off = np.asarray(offsets, np.int64)
+    G = off.size
+    if pairs is None:
+        pairs = [(g, k) for g in range(G) for k in range(K)]
+
+    def explain(flat):
+        vals, mags = [], []
+        for f in np.asarray(flat):
+            g, k = pairs[f // N]
+            n = int(f % N)
+            lo = 0 if g == 0 else int(off[g - 1])
+            hi = int(off[g])
+            ks = lo - lo % 32
+            a = np.zeros(hi - ks, np.uint8)
+            b = np.zeros(hi - ks, np.uint8)
+            a[lo - ks:] = xt[k, lo:hi]
+            b[lo - ks:] = dyt[n, lo:hi]
+            blk = np.arange(ks, hi) // 32
+            v, mag = model_dot(a, b, k0=ks, sa=np.exp2(xe[k, blk] - 127),
+                               sb=np.exp2(de[n, blk] - 127))
+            vals.append(v)
+            mags.append(mag)
+        return np.array(vals), np.array(mags)
+    return explain
