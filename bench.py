@@ -12,12 +12,16 @@ Next rows, timed in passes of their own after the step and reported under "next_
 Default workload: the DeepSeek-V3-shaped local expert slice (32 experts, hidden 7168,
 intermediate 2048, 16384 routed token rows, Zipf(1.1) group sizes), e4m3fn.
 
-Timing: W untimed warm-up steps, then exactly K timed steps between device synchronisations;
-every operation is also bracketed with HIP events on the stream it runs on, giving per-launch
-averages.  The JSON line reports whole-step throughput (algorithmic GEMM flops of the step per
-second of step time, quantization time included), the quantizers' aggregate GB/s, the GEMMs'
-TFLOP/s, a roofline entry for the step kernel that takes the most time, and the CPU oracle timed
-on a bounded sample on the host.
+Timing: W untimed warm-up steps, then exactly K timed steps between device synchronisations
+(the step time and `value`); every operation is bracketed with HIP events on the stream it runs
+on, giving per-launch warm averages (us_warm).  Each operation is then timed again K times with
+a 1 GiB cache flush before every launch (us, the median: inputs come from HBM, not from the
+L2s or the 256 MB last-level cache).  The JSON line reports whole-step throughput (algorithmic
+GEMM flops of the step per second of step time, quantization time included), per-op flushed
+and warm times with GB/s or TFLOP/s and % of peak, the same for the other configurations
+(tiny in e4m3fnuz, the dense Llama3-8B FFN GEMM, DeepSeek-MoE-16B experts, the DeepSeek-V3
+slice in e4m3fnuz), a roofline entry for the step kernel that takes the most time, and the CPU
+oracle timed on the host at all threads and at one thread.
 """
 from __future__ import annotations
 
@@ -53,6 +57,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the further configurations timed after the headline workload")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy 4 times (reference for the HBM "
@@ -73,13 +79,15 @@ def copy_calibration(torch):
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 4}), flush=True)
 
 
-def make_inputs(name, torch, dev):
+def make_inputs(name, torch, dev, fmt=None, ops=None):
     """Device-resident synthetic inputs.  Group offsets come from the seeded numpy recipe of the
     workloads module; the bf16 tensors are drawn on the device with a seeded generator (same
     distributions as the recipe: X, dY ~ N(0,1), W ~ N(0, 0.02); the tiny workload adds 1% x50
-    outliers)."""
+    outliers).  fmt / ops override the workload's encoding and operation list."""
     import workloads
-    cfg_name, fmt, ops = WORKLOADS[name]
+    cfg_name, fmt0, ops0 = WORKLOADS[name]
+    fmt = fmt0 if fmt is None else fmt
+    ops = ops0 if ops is None else ops
     cfg = workloads.CONFIGS[cfg_name]
     M, K, N, E = cfg["M"], cfg["K"], cfg["N"], cfg["E"]
     rng = np.random.Generator(np.random.PCG64(cfg["seed"]))
@@ -263,35 +271,71 @@ class Step:
         return seq, extra
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(d, seconds):
-    """The oracle (never tuned) on the host: forward grouped GEMM rows of the same shapes,
-    on a row sample sized to roughly `seconds` of work, plus rowwise quant GB/s."""
+    """The oracle (never tuned) on the host, at all its threads and at one thread:
+      - forward grouped GEMM rows of the workload's shapes (N x K), on a row sample sized to
+        roughly `seconds` of work (all threads) or a quarter of it (one thread);
+      - rowwise quantization of a full-size [M, N] gradient matrix (dY's shape) at both thread
+        counts, and of the full [M, K] activations at all threads."""
     import oracle
     import workloads
-    K, N, fmt = d["K"], d["N"], d["fmt"]
-    rng_seed = 1234
-    xs = workloads.make_matrix(rng_seed, 1024, K, 1.0, 0.0)
-    ws = workloads.make_matrix(rng_seed + 1, K, N, 0.02)
-    t0 = time.perf_counter()
+    M, K, N, fmt = d["M"], d["K"], d["N"], d["fmt"]
+    all_threads = oracle.num_threads()
+    xs = workloads.make_matrix(1234, 1024, K, 1.0, 0.0)
+    ws = workloads.make_matrix(1235, K, N, 0.02)
     qa, sa = oracle.quant_rowwise(xs, fmt)
-    tq = time.perf_counter() - t0
     qbt, sb = oracle.quant_colwise_grouped(ws, np.array([K], np.int32), fmt)
     off = np.array([qa.shape[0]], np.int32)
-    # calibrate on as many rows as the oracle has threads (fewer would leave threads idle and
-    # overstate the time per row), then run a sample sized to the time budget
-    ncal = max(4, min(1024, oracle.num_threads()))
-    t0 = time.perf_counter()
-    oracle.gemm_fwd_rows(fmt, qa, sa, qbt, K, 0, sb, off, N, K, np.arange(ncal))
-    tcal = time.perf_counter() - t0
-    nrows = int(max(4, min(1024, ncal * seconds / max(tcal, 1e-6))))
-    t0 = time.perf_counter()
-    oracle.gemm_fwd_rows(fmt, qa, sa, qbt, K, 0, sb, off, N, K, np.arange(nrows))
-    tg = time.perf_counter() - t0
-    return dict(value=2.0 * nrows * N * K / tg / 1e12, unit="TFLOP/s", cores=oracle.num_threads(),
-                kind="oracle",
-                sample=(f"forward grouped GEMM, {nrows} rows x N={N} x K={K} ({tg:.1f} s); "
-                        f"rowwise quant of 1024x{K} bf16 at {1024 * K * 3 / tq / 1e9:.3f} GB/s"),
-                quant_GBps=1024 * K * 3 / tq / 1e9)
+
+    def gemm_rate(threads, budget):
+        oracle.set_num_threads(threads)
+        # calibrate on as many rows as threads (fewer would leave threads idle), then a sample
+        # sized to the budget
+        ncal = max(2, min(1024, threads))
+        t0 = time.perf_counter()
+        oracle.gemm_fwd_rows(fmt, qa, sa, qbt, K, 0, sb, off, N, K, np.arange(ncal))
+        tcal = time.perf_counter() - t0
+        nrows = int(max(2, min(1024, ncal * budget / max(tcal, 1e-6))))
+        t0 = time.perf_counter()
+        oracle.gemm_fwd_rows(fmt, qa, sa, qbt, K, 0, sb, off, N, K, np.arange(nrows))
+        tg = time.perf_counter() - t0
+        return 2.0 * nrows * N * K / tg / 1e12, nrows, tg
+
+    def quant_rate(threads, rows, cols):
+        oracle.set_num_threads(threads)
+        x = workloads.make_matrix(1236, rows, cols, 1.0, 0.0)
+        t0 = time.perf_counter()
+        oracle.quant_rowwise(x, fmt)
+        tq = time.perf_counter() - t0
+        return rows * cols * 3 / tq / 1e9, tq
+
+    try:
+        tf_all, rows_all, tg_all = gemm_rate(all_threads, seconds)
+        tf_one, rows_one, tg_one = gemm_rate(1, seconds / 4)
+        qdy_all, _ = quant_rate(all_threads, M, N)
+        qdy_one, tq_one = quant_rate(1, M, N)
+        qx_all, _ = quant_rate(all_threads, M, K)
+    finally:
+        oracle.set_num_threads(all_threads)
+    return dict(
+        value=tf_all, unit="TFLOP/s", cores=all_threads, kind="oracle",
+        sample=(f"forward grouped GEMM rows at N={N}, K={K}: {rows_all} rows at {all_threads} "
+                f"threads ({tg_all:.1f} s), {rows_one} rows at 1 thread ({tg_one:.1f} s); rowwise "
+                f"quant of the full {M}x{N} and {M}x{K} bf16 matrices"),
+        value_1thread=tf_one, cpu_model=cpu_model(), nproc=os.cpu_count(),
+        omp_num_threads=os.environ.get("OMP_NUM_THREADS"),
+        quant_GBps={f"{M}x{N}": {"threads_all": round(qdy_all, 4), "threads_1": round(qdy_one, 4)},
+                    f"{M}x{K}": {"threads_all": round(qx_all, 4)}})
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_dsv3_step.md")
@@ -326,7 +370,7 @@ def measured_traffic(kernel):
 
 def time_passes(torch, seq, warmup, steps):
     """Average per-op milliseconds over `steps` passes of `seq` after `warmup` passes, each op
-    bracketed by HIP events on the stream it runs on."""
+    bracketed by HIP events on the stream it runs on (warm: inputs may sit in the caches)."""
     if not seq:
         return {}
     for _ in range(warmup):
@@ -344,6 +388,77 @@ def time_passes(torch, seq, warmup, steps):
             evs[name].append((a, b))
     torch.cuda.synchronize()
     return {n: float(np.mean([a.elapsed_time(b) for a, b in v])) for n, v in evs.items()}
+
+
+class Flush:
+    """Writes a 1 GiB buffer: evicts the 8 L2s (4 MB each) and the 256 MB last-level cache, so
+    that the next kernel reads its inputs from HBM."""
+
+    def __init__(self, torch, dev):
+        self.buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        self.v = 0
+
+    def __call__(self):
+        self.v ^= 1
+        self.buf.fill_(self.v)
+
+
+def time_flushed(torch, seq, steps, flush):
+    """Median per-op milliseconds over `steps` launches, each launch preceded by a cache flush
+    (outside its events)."""
+    if not seq:
+        return {}
+    evs = {name: [] for name, _ in seq}
+    for _ in range(steps):
+        for name, fn in seq:
+            flush()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            evs[name].append((a, b))
+    torch.cuda.synchronize()
+    return {n: float(np.median([a.elapsed_time(b) for a, b in v])) for n, v in evs.items()}
+
+
+def entry(st, n, ms, ms_warm=None):
+    """Per-op record: flushed microseconds and their throughput (% of peak); warm beside."""
+    ent = {"us": round(ms * 1e3, 2)}
+    if ms_warm is not None:
+        ent["us_warm"] = round(ms_warm * 1e3, 2)
+    if n in st.flops:
+        tf = st.flops[n] / (ms * 1e-3) / 1e12
+        ent.update(TFLOPs=round(tf, 1), frac_mfma_peak=round(tf / FP8_PEAK_TFLOPS, 4))
+        gb = st.gemm_bytes[n] / (ms * 1e-3) / 1e9
+        ent.update(GBps=round(gb, 1), frac_hbm_peak=round(gb / HBM_PEAK_GBPS, 4))
+    if n in st.bytes:
+        gb = st.bytes[n] / (ms * 1e-3) / 1e9
+        ent.update(GBps=round(gb, 1), frac_hbm_peak=round(gb / HBM_PEAK_GBPS, 4))
+    return ent
+
+
+# Further configurations timed after the headline workload (per-op flushed and warm times):
+# name -> (workload, format, ops)
+EXTRA_CONFIGS = {
+    "tiny_e4m3fnuz": ("tiny", 0, ("fwd", "wgrad")),
+    "dense_llama3_8b_ffn": ("dense", 1, ("fwd",)),
+    "moe16b": ("moe16b", 1, ("fwd",)),
+    "dsv3_e4m3fnuz": ("dsv3", 0, ("fwd", "wgrad")),
+}
+
+
+def run_config(fq, torch, dev, name, fmt, ops, warmup, steps, flush):
+    d = make_inputs(name, torch, dev, fmt=fmt, ops=ops)
+    st = Step(fq, torch, d)
+    seq, extra = st.ops()
+    seq = seq + extra
+    warm = time_passes(torch, seq, warmup, steps)
+    cold = time_flushed(torch, seq, steps, flush)
+    out = {n: entry(st, n, cold[n], warm[n]) for n in cold}
+    del st, d
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -384,45 +499,45 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    per_op = {n: float(np.mean([a.elapsed_time(b) for a, b in v])) for n, v in evs.items()}
-    extra_op = time_passes(torch, extra, args.warmup, args.steps)
+    warm_op = {n: float(np.mean([a.elapsed_time(b) for a, b in v])) for n, v in evs.items()}
+    warm_extra = time_passes(torch, extra, args.warmup, args.steps)
+    flush = Flush(torch, dev)
+    cold_op = time_flushed(torch, seq, args.steps, flush)
+    cold_extra = time_flushed(torch, extra, args.steps, flush)
 
-    def entry(n, ms):
-        ent = {"us": round(ms * 1e3, 2)}
-        if n in st.flops:
-            tf = st.flops[n] / (ms * 1e-3) / 1e12
-            ent.update(TFLOPs=round(tf, 1), frac_mfma_peak=round(tf / FP8_PEAK_TFLOPS, 4))
-            gb = st.gemm_bytes[n] / (ms * 1e-3) / 1e9
-            ent.update(GBps=round(gb, 1), frac_hbm_peak=round(gb / HBM_PEAK_GBPS, 4))
-        if n in st.bytes:
-            gb = st.bytes[n] / (ms * 1e-3) / 1e9
-            ent.update(GBps=round(gb, 1), frac_hbm_peak=round(gb / HBM_PEAK_GBPS, 4))
-        return ent
-
-    kernels = {n: entry(n, ms) for n, ms in per_op.items()}
-    next_rows = {n: entry(n, ms) for n, ms in extra_op.items()}
-    gemm_ms = sum(per_op[n] for n in per_op if n in st.flops)
-    quant_ms = sum(per_op[n] for n in per_op if n in st.bytes)
-    total_flops = sum(st.flops[n] for n in per_op if n in st.flops)
-    total_bytes = sum(st.bytes[n] for n in per_op if n in st.bytes)
+    kernels = {n: entry(st, n, cold_op[n], warm_op[n]) for n in cold_op}
+    next_rows = {n: entry(st, n, cold_extra[n], warm_extra[n]) for n in cold_extra}
+    gemm_ms = sum(cold_op[n] for n in cold_op if n in st.flops)
+    quant_ms = sum(cold_op[n] for n in cold_op if n in st.bytes)
+    total_flops = sum(st.flops[n] for n in cold_op if n in st.flops)
+    total_bytes = sum(st.bytes[n] for n in cold_op if n in st.bytes)
     value = total_flops / (ms_step * 1e-3) / 1e12
 
-    dom = max(per_op, key=per_op.get)
+    dom = max(cold_op, key=cold_op.get)
     # a GEMM is bound by whichever peak gives the longer ideal time: the weight-gradient GEMM's
     # bf16 output (groups x K x N) makes it HBM-bound on these shapes
     gemm_hbm_bound = (dom in st.flops and st.gemm_bytes[dom] / (HBM_PEAK_GBPS * 1e9)
                       > st.flops[dom] / (FP8_PEAK_TFLOPS * 1e12))
     if dom in st.flops and not gemm_hbm_bound:
-        ach = st.flops[dom] / (per_op[dom] * 1e-3) / 1e12
+        ach = st.flops[dom] / (cold_op[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / FP8_PEAK_TFLOPS, 4)}
     else:
         nbytes = st.gemm_bytes[dom] if dom in st.flops else st.bytes[dom]
-        ach = nbytes / (per_op[dom] * 1e-3) / 1e9
+        ach = nbytes / (cold_op[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4)}
     roof["kernel"] = dom
+    roof["timing"] = "median of flushed launches"
     roof["traffic"] = measured_traffic(dom)
+
+    configs = {}
+    if args.workload == "dsv3" and not args.no_configs:
+        del st, seq, extra
+        torch.cuda.empty_cache()
+        for cname, (wl, cfmt, cops) in EXTRA_CONFIGS.items():
+            configs[cname] = run_config(fq, torch, dev, wl, cfmt, cops, args.warmup,
+                                        max(5, args.steps // 2), flush)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -448,12 +563,15 @@ def main():
         "data": "synthetic (seeded; device-drawn N(0,1) activations/gradients, N(0,0.02) "
                 "weights; Zipf-routed group offsets)",
         "config": cfg,
+        "timing": "per-op us: median of launches each preceded by a 1 GiB cache flush; us_warm: "
+                  "mean inside the timed steps",
         "quantize_GBps": round(total_bytes / (quant_ms * 1e-3) / 1e9, 1),
         "quantize_frac_hbm_peak": round(total_bytes / (quant_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "gemm_TFLOPs": round(total_flops / (gemm_ms * 1e-3) / 1e12, 1),
         "gemm_frac_mfma_peak": round(total_flops / (gemm_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
         "kernels": kernels,
         "next_rows": next_rows,
+        "configs": configs,
         "roofline": roof,
         "cpu_baseline": cpu,
     }
