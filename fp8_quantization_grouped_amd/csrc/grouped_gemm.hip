@@ -37,10 +37,11 @@
 //     block sums in fp32 (measured on gfx950; the same for the older fp8 instruction).
 //
 // e4m3fnuz operands: the matrix cores read OCP e4m3 only (byte 0x7F, the fnuz 240 code, is NaN
-// there), so fnuz fragments are re-encoded to the e4m3fn byte of the same value after the LDS
-// read: exponent field - 1 for fnuz exponents >= 2 (exact), and the nearest e4m3fn subnormal
-// (ties to even) for fnuz values below 2^-6, which moves a product by at most 2^-10
-// quantization units.
+// there), so fnuz bytes are re-encoded in LDS, once per step by the lanes that loaded them, to
+// the e4m3fn byte of the same value: exponent field - 1 for fnuz exponents >= 2 (exact), and
+// the nearest e4m3fn subnormal (ties to even) for fnuz values below 2^-6, which moves a product
+// by at most 2^-10 quantization units.  (Re-encoding every fragment after its LDS read instead
+// costs each wave ~12 VALU operations per fragment dword: the e4m3fnuz GEMMs ran 4x slower.)
 //
 // Weight gradient: a group's token range starts and ends anywhere, so the chunk holding the
 // first (last) token of the group can carry neighbouring groups' bytes; those bytes of the
@@ -587,6 +588,25 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
             const int cur_st = (stage0 + (kk & 1)) & 1;
             const int kpos = cur.kstart + kk * GK;
             wait_vm0();  // this wave's loads of step kk have landed
+            if (FNUZ) {
+                // e4m3fnuz operands: each lane re-encodes the 16-byte chunks it brought into
+                // the stage to the e4m3fn bytes of the same values, in place, before the
+                // barrier that publishes the stage (once per byte, not once per fragment read)
+#pragma unroll
+                for (int i = 0; i < NP; i++) {
+                    const int slot = (wave * NP + i) * 1024 + lane * 16;
+                    if (MODE == MODE_WGRAD || wave * 8 * NP + 8 * i < cur.a_rows) {
+                        uint4* q = reinterpret_cast<uint4*>(&smem[cur_st][0][slot]);
+                        uint4 w = *q;
+                        *q = make_uint4(fnuz_to_fn4(w.x), fnuz_to_fn4(w.y), fnuz_to_fn4(w.z),
+                                        fnuz_to_fn4(w.w));
+                    }
+                    uint4* q = reinterpret_cast<uint4*>(&smem[cur_st][1][slot]);
+                    uint4 w = *q;
+                    *q = make_uint4(fnuz_to_fn4(w.x), fnuz_to_fn4(w.y), fnuz_to_fn4(w.z),
+                                    fnuz_to_fn4(w.w));
+                }
+            }
             if (MXV == MX_BYTES && scales_pending) {
                 commit_scales(cur_st);  // read after this step's barrier
                 scales_pending = false;
@@ -656,7 +676,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
 #pragma unroll
             for (int j = 0; j < NJ; j++) {
                 const int rn = wn * WNC + brow(j, lr);
-                bf[j] = frag<true>(Bs, rn, kg, FNUZ);
+                bf[j] = frag<true>(Bs, rn, kg, false);
                 // scale bytes are read unconditionally (in-range LDS) and then selected: a
                 // conditional read becomes a branch per row, and the compiler then gathers all
                 // fragment reads ahead of the matrix instructions (registers spill)
@@ -675,7 +695,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
 #pragma unroll
             for (int i = 0; i < 8; i++) {
                 const int rm = wm * 128 + i * 16 + lr;
-                const v8i_t af = frag<false>(As, rm, kg, FNUZ);
+                const v8i_t af = frag<false>(As, rm, kg, false);
                 if (pend && !MX && NW == 4 && i < NP / 2) {  // two parts per row in the first rows
                     part(P, 2 * i);
                     part(P, 2 * i + 1);
