@@ -41,6 +41,8 @@ SIGNATURES = {
     "fp8_quant_colwise_grouped_workspace_size": (_SZ, [_I64, _I64, _I32]),
     "fp8_quant_colwise_grouped": (_I, [_P, _I64, _I64, _I64, _P, _I32, _I, _P, _I64, _P, _P, _SZ,
                                        _P]),
+    "fp8_quant_colwise_grouped_noalloc": (_I, [_P, _I64, _I64, _I64, _P, _I32, _I, _P, _I64, _P,
+                                               _P]),
     "fp8_quant_weights_dual_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "fp8_quant_weights_dual": (_I, [_P, _I64, _I64, _I64, _I64, _I, _P, _I64, _P, _P, _I64, _P, _P,
                                     _SZ, _P]),
@@ -155,6 +157,29 @@ def fp8_quant_colwise_grouped(x: torch.Tensor, offsets: torch.Tensor, fmt: int,
                                          fmt, _ptr(q_t), q_t.stride(0), _ptr(scales),
                                          _ptr(workspace), workspace.numel(), _stream(x))
     _check("fp8_quant_colwise_grouped", st)
+    return q_t, scales
+
+
+def fp8_quant_colwise_grouped_noalloc(x: torch.Tensor, offsets: torch.Tensor, fmt: int,
+                                      q_t: torch.Tensor | None = None,
+                                      scales: torch.Tensor | None = None):
+    """fp8_quant_colwise_grouped through the entry point that allocates nothing (its maxima
+    live in the library's static per-GPU array; sizes beyond it raise).  The C call allocates
+    nothing; pass q_t and scales to allocate nothing here either."""
+    _dev(x, "x")
+    _dev(offsets, "offsets")
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    assert offsets.dtype == torch.int32 and offsets.is_contiguous()
+    rows, cols = x.shape
+    groups = offsets.numel()
+    if q_t is None:
+        q_t = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((groups, cols), dtype=torch.float32, device=x.device)
+    st = lib().fp8_quant_colwise_grouped_noalloc(_ptr(x), rows, cols, x.stride(0), _ptr(offsets),
+                                                 groups, fmt, _ptr(q_t), q_t.stride(0),
+                                                 _ptr(scales), _stream(x))
+    _check("fp8_quant_colwise_grouped_noalloc", st)
     return q_t, scales
 
 

@@ -29,6 +29,8 @@
 // search in LDS instead of a chain of dependent global loads.  The block whose tile contains
 // a group's first row writes that group's scales; the last row tile also writes groups that
 // start at the end (trailing empty groups).
+#include <mutex>
+
 #include "common.hpp"
 
 namespace fp8q {
@@ -644,12 +646,13 @@ extern "C" size_t fp8_quant_colwise_grouped_workspace_size(int64_t rows, int64_t
     return (b + 255) & ~(size_t)255;
 }
 
-extern "C" fp8q_status_t fp8_quant_colwise_grouped(const uint16_t* x, int64_t rows, int64_t cols,
-                                                   int64_t ld_x, const int32_t* offsets,
-                                                   int32_t groups, fp8q_format_t fmt,
-                                                   uint8_t* q_t, int64_t ld_qt, float* scales,
-                                                   void* workspace, size_t workspace_bytes,
-                                                   hipStream_t stream) {
+namespace fp8q {
+
+// Argument checks and dispatch shared by both colwise entry points.
+static fp8q_status_t colwise_entry(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                   const int32_t* offsets, int32_t groups, fp8q_format_t fmt,
+                                   uint8_t* q_t, int64_t ld_qt, float* scales, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
     if (rows < 0 || cols < 0 || groups < 1 || ld_x < cols || ld_qt < rows || !fp8q_fmt_ok(fmt))
         return FP8Q_ERR_INVALID_ARG;
     if (!offsets) return FP8Q_ERR_INVALID_ARG;
@@ -657,15 +660,64 @@ extern "C" fp8q_status_t fp8_quant_colwise_grouped(const uint16_t* x, int64_t ro
     if (!scales || (rows > 0 && (!x || !q_t))) return FP8Q_ERR_INVALID_ARG;
     const size_t need = fp8_quant_colwise_grouped_workspace_size(rows, cols, groups);
     if (workspace_bytes < need || !workspace) return FP8Q_ERR_WORKSPACE;
-    if ((rows + fp8q::CW_TR - 1) / fp8q::CW_TR > 0x7FFFFFFFLL ||
-        (cols + fp8q::CW_TC - 1) / fp8q::CW_TC > 65535)
+    if ((rows + CW_TR - 1) / CW_TR > 0x7FFFFFFFLL || (cols + CW_TC - 1) / CW_TC > 65535)
         return FP8Q_ERR_UNSUPPORTED;
     uint32_t* ws = static_cast<uint32_t*>(workspace);
     if (fmt == FP8Q_E4M3FN)
-        return fp8q::colwise_run<FP8Q_E4M3FN>(x, rows, cols, ld_x, offsets, groups, q_t, ld_qt,
-                                              scales, ws, stream);
-    return fp8q::colwise_run<FP8Q_E4M3FNUZ>(x, rows, cols, ld_x, offsets, groups, q_t, ld_qt,
-                                            scales, ws, stream);
+        return colwise_run<FP8Q_E4M3FN>(x, rows, cols, ld_x, offsets, groups, q_t, ld_qt, scales,
+                                        ws, stream);
+    return colwise_run<FP8Q_E4M3FNUZ>(x, rows, cols, ld_x, offsets, groups, q_t, ld_qt, scales,
+                                      ws, stream);
+}
+
+// Cross-block maxima of fp8_quant_colwise_grouped_noalloc: one array per GPU, held until the
+// process ends.  In host code this name is only a stand-in for the device symbol, never an
+// address: the device address of each GPU's copy comes from hipGetSymbolAddress, taken once per
+// device with that device current, and is what the kernels receive.
+static __device__ __align__(256) uint32_t scratch[FP8Q_NOALLOC_SCRATCH_BYTES / sizeof(uint32_t)];
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];
+
+static fp8q_status_t noalloc_scratch(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return FP8Q_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FP8Q_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return FP8Q_OK;
+}
+
+}  // namespace fp8q
+
+extern "C" fp8q_status_t fp8_quant_colwise_grouped(const uint16_t* x, int64_t rows, int64_t cols,
+                                                   int64_t ld_x, const int32_t* offsets,
+                                                   int32_t groups, fp8q_format_t fmt,
+                                                   uint8_t* q_t, int64_t ld_qt, float* scales,
+                                                   void* workspace, size_t workspace_bytes,
+                                                   hipStream_t stream) {
+    return fp8q::colwise_entry(x, rows, cols, ld_x, offsets, groups, fmt, q_t, ld_qt, scales,
+                               workspace, workspace_bytes, stream);
+}
+
+extern "C" fp8q_status_t fp8_quant_colwise_grouped_noalloc(const uint16_t* x, int64_t rows,
+                                                           int64_t cols, int64_t ld_x,
+                                                           const int32_t* offsets,
+                                                           int32_t groups, fp8q_format_t fmt,
+                                                           uint8_t* q_t, int64_t ld_qt,
+                                                           float* scales, hipStream_t stream) {
+    // sizes beyond the static array are rejected before anything else touches the device
+    if (cols > 0 && groups >= 1 &&
+        fp8_quant_colwise_grouped_workspace_size(rows, cols, groups) > FP8Q_NOALLOC_SCRATCH_BYTES)
+        return FP8Q_ERR_WORKSPACE;
+    void* ws = nullptr;
+    const fp8q_status_t st = fp8q::noalloc_scratch(&ws);
+    if (st != FP8Q_OK) return st;
+    return fp8q::colwise_entry(x, rows, cols, ld_x, offsets, groups, fmt, q_t, ld_qt, scales, ws,
+                               FP8Q_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 extern "C" size_t fp8_quant_weights_dual_workspace_size(int64_t experts, int64_t K, int64_t N) {

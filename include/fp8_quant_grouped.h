@@ -137,6 +137,23 @@ fp8q_status_t fp8_quant_colwise_grouped(const uint16_t* x, int64_t rows, int64_t
                                         float* scales, void* workspace, size_t workspace_bytes,
                                         hipStream_t stream);
 
+/* fp8_quant_colwise_grouped without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments (minus the workspace), results and
+ * errors as fp8_quant_colwise_grouped, bit for bit.  Its cross-block maxima live in a static
+ * device array of FP8Q_NOALLOC_SCRATCH_BYTES (8 MiB) per GPU, held until the process ends; a
+ * call whose fp8_quant_colwise_grouped_workspace_size(rows, cols, groups) exceeds it returns
+ * FP8Q_ERR_WORKSPACE and launches nothing.  Every call on a GPU shares that GPU's array (each
+ * call clears what it uses on its stream): calls that overlap on one GPU -- on different
+ * streams, or from several host threads -- race and must be serialised by the caller.  The
+ * first call on a device looks up the array's device address (hipGetSymbolAddress) and keeps
+ * it; a failure there returns FP8Q_ERR_HIP. */
+#define FP8Q_NOALLOC_SCRATCH_BYTES (8u << 20)
+fp8q_status_t fp8_quant_colwise_grouped_noalloc(const uint16_t* x, int64_t rows, int64_t cols,
+                                                int64_t ld_x, const int32_t* offsets,
+                                                int32_t groups, fp8q_format_t fmt, uint8_t* q_t,
+                                                int64_t ld_qt, float* scales, hipStream_t stream);
+
 /* Expert weights in both layouts at once, for quantizing them once per optimizer step and
  * reusing the bytes across micro-batches (the forward reads W^T per expert with one scale per
  * (expert, output column); the data gradient reads W along N with one scale per (expert, k)).
