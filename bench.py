@@ -138,7 +138,10 @@ class Step:
                 xqt=e(K, ldm), sxg=e(G, K, dt=f32), dyqt=e(N, ldm), sdyg=e(G, N, dt=f32),
                 dw=e(G, K, N, dt=bf),
                 ws_x=e(max(256, fq.fp8_quant_colwise_grouped_workspace_size(M, K, G))),
-                ws_dy=e(max(256, fq.fp8_quant_colwise_grouped_workspace_size(M, N, G))))
+                ws_dy=e(max(256, fq.fp8_quant_colwise_grouped_workspace_size(M, N, G))),
+                # both layouts of X and of dY in one call each (rowwise + transposed)
+                dxq=e(M, K), dxs=e(M, dt=f32), dyq2=e(M, N), dys2=e(M, dt=f32),
+                ws_dual=e(max(256, fq.fp8_quant_dual_grouped_workspace_size(M, K, G))))
         if "gather" in d["ops"]:
             # dispatch in expert order: 2048 tokens x top-8 over 32 experts (seeded Zipf routing)
             import workloads
@@ -177,6 +180,9 @@ class Step:
             self.gemm_bytes["gemm_wgrad"] = K * M + N * M + G * K * N * 2 + G * K * 4 + G * N * 4
             self.bytes["quant_colwise_xT"] = M * K * 3 + G * K * 4
             self.bytes["quant_colwise_dyT"] = M * N * 3 + G * N * 4
+            # algorithmic: read once, both FP8 layouts written, both scale sets
+            self.bytes["quant_dual_x"] = M * K * 4 + M * 4 + G * K * 4
+            self.bytes["quant_dual_dy"] = M * N * 4 + M * 4 + G * N * 4
         if "mxwgrad" in d["ops"]:
             self.flops["gemm_mx_wgrad"] = 2.0 * M * N * K
             self.gemm_bytes["gemm_mx_wgrad"] = (K * M + N * M + G * K * N * 2 + K * M // 32
@@ -230,6 +236,17 @@ class Step:
                 ("gemm_wgrad", lambda: fq.fp8_grouped_gemm(
                     fq.GEMM_WGRAD_KGROUPED, fmt, b["xqt"], b["sxg"], b["dyqt"], b["sdyg"],
                     d["offsets"], M, N, K, ldb=self.ldm, c=b["dw"], workspace=b["gws"])),
+            ]
+        if "wgrad" in d["ops"]:
+            # both layouts at once: X for the forward and the weight gradient, dY for the data
+            # gradient and the weight gradient (compare with the rowwise + transposed calls)
+            extra += [
+                ("quant_dual_x", lambda: fq.fp8_quant_dual_grouped(
+                    d["x"], d["offsets"], fmt, q=b["dxq"], s_rows=b["dxs"], q_t=b["xqt"][:, :M],
+                    s_cols=b["sxg"], workspace=b["ws_dual"])),
+                ("quant_dual_dy", lambda: fq.fp8_quant_dual_grouped(
+                    d["dy"], d["offsets"], fmt, q=b["dyq2"], s_rows=b["dys2"],
+                    q_t=b["dyqt"][:, :M], s_cols=b["sdyg"], workspace=b["ws_dual"])),
             ]
         if "dgrad" in d["ops"]:
             # dX[m, k] = sum_n dY[m, n] W_g[k, n]: the forward mode with W's [K, N] rows of expert

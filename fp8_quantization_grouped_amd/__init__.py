@@ -41,6 +41,9 @@ SIGNATURES = {
     "fp8_quant_colwise_grouped_workspace_size": (_SZ, [_I64, _I64, _I32]),
     "fp8_quant_colwise_grouped": (_I, [_P, _I64, _I64, _I64, _P, _I32, _I, _P, _I64, _P, _P, _SZ,
                                        _P]),
+    "fp8_quant_dual_grouped_workspace_size": (_SZ, [_I64, _I64, _I32]),
+    "fp8_quant_dual_grouped": (_I, [_P, _I64, _I64, _I64, _P, _I32, _I, _P, _I64, _P, _P, _I64, _P,
+                                    _P, _SZ, _P]),
     "fp8_quant_colwise_grouped_noalloc": (_I, [_P, _I64, _I64, _I64, _P, _I32, _I, _P, _I64, _P,
                                                _P]),
     "fp8_quant_weights_dual_workspace_size": (_SZ, [_I64, _I64, _I64]),
@@ -158,6 +161,38 @@ def fp8_quant_colwise_grouped(x: torch.Tensor, offsets: torch.Tensor, fmt: int,
                                          _ptr(workspace), workspace.numel(), _stream(x))
     _check("fp8_quant_colwise_grouped", st)
     return q_t, scales
+
+
+def fp8_quant_dual_grouped_workspace_size(rows: int, cols: int, groups: int) -> int:
+    return int(lib().fp8_quant_dual_grouped_workspace_size(rows, cols, groups))
+
+
+def fp8_quant_dual_grouped(x: torch.Tensor, offsets: torch.Tensor, fmt: int,
+                           q: torch.Tensor | None = None, s_rows: torch.Tensor | None = None,
+                           q_t: torch.Tensor | None = None, s_cols: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None):
+    """Both layouts of x [rows, cols] at once: returns ((q uint8 [rows, cols], s_rows float32
+    [rows]) as fp8_quant_rowwise would, (q_t uint8 [cols, rows], s_cols float32 [groups, cols])
+    as fp8_quant_colwise_grouped with these token offsets would)."""
+    _dev(x, "x")
+    _dev(offsets, "offsets")
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    assert offsets.dtype == torch.int32 and offsets.is_contiguous()
+    rows, cols = x.shape
+    groups = offsets.numel()
+    e = lambda *s, dt=torch.uint8: torch.empty(s, dtype=dt, device=x.device)
+    q = e(rows, cols) if q is None else q
+    s_rows = e(rows, dt=torch.float32) if s_rows is None else s_rows
+    q_t = e(cols, rows) if q_t is None else q_t
+    s_cols = e(groups, cols, dt=torch.float32) if s_cols is None else s_cols
+    need = fp8_quant_dual_grouped_workspace_size(rows, cols, groups)
+    if workspace is None:
+        workspace = e(max(need, 256))
+    st = lib().fp8_quant_dual_grouped(_ptr(x), rows, cols, x.stride(0), _ptr(offsets), groups, fmt,
+                                      _ptr(q), q.stride(0), _ptr(s_rows), _ptr(q_t), q_t.stride(0),
+                                      _ptr(s_cols), _ptr(workspace), workspace.numel(), _stream(x))
+    _check("fp8_quant_dual_grouped", st)
+    return (q, s_rows), (q_t, s_cols)
 
 
 def fp8_quant_colwise_grouped_noalloc(x: torch.Tensor, offsets: torch.Tensor, fmt: int,

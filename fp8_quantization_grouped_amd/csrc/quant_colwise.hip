@@ -123,11 +123,14 @@ __global__ void cw_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
         p[i] = 0u;
 }
 
-template <bool VEC, bool LDS, bool NT>
+// ROWP: also write each row's maximum over the tile's 64 columns (bf16 magnitude bits) to
+// rowp[r * gridDim.y + blockIdx.y]: the dual-layout call reduces them into rowwise scales.
+template <bool VEC, bool LDS, bool NT, bool ROWP = false>
 __global__ __launch_bounds__(256) void colwise_amax_kernel(const uint16_t* __restrict__ x,
                                                            int64_t R, int64_t C, int64_t ld_x,
                                                            const int32_t* __restrict__ offsets,
-                                                           int G, uint32_t* __restrict__ amax) {
+                                                           int G, uint32_t* __restrict__ amax,
+                                                           uint16_t* __restrict__ rowp) {
     const int t = threadIdx.x, o = t & 7, qd = t >> 3, lane = t & 63, wave = t >> 6;
     const int64_t rb = (int64_t)blockIdx.x * CW_TR * CW_TPB, c0 = (int64_t)blockIdx.y * CW_TC;
     __shared__ uint32_t red[4][8][4];
@@ -170,6 +173,20 @@ __global__ __launch_bounds__(256) void colwise_amax_kernel(const uint16_t* __res
         if (r0 >= R) break;  // block-uniform
         if (k + 1 < CW_TPB) cw_load<VEC, NT>(x, R, C, ld_x, r0 + CW_TR, c0, o, qd, vn);
         const int64_t r_end = r0 + CW_TR < R ? r0 + CW_TR : R;
+        if (ROWP) {
+            // the 8 lanes of a row group (o = 0..7, consecutive lanes) hold its 64 columns
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                uint32_t m = pk_max_u16(pk_max_u16(mag2(v[i].x), mag2(v[i].y)),
+                                        pk_max_u16(mag2(v[i].z), mag2(v[i].w)));
+                m = hmax16(m);
+                m = max(m, (uint32_t)__shfl_xor((int)m, 1, 64));
+                m = max(m, (uint32_t)__shfl_xor((int)m, 2, 64));
+                m = max(m, (uint32_t)__shfl_xor((int)m, 4, 64));
+                const int64_t r = r0 + 8 * qd + i;
+                if (o == 0 && r < R) rowp[r * (int64_t)gridDim.y + blockIdx.y] = (uint16_t)m;
+            }
+        }
         const int g_first = off.group_of(r0);
         const int g_last = off.group_of(r_end - 1);
         for (int g = g_first; g <= g_last; g++) {
@@ -199,11 +216,14 @@ __global__ __launch_bounds__(256) void colwise_amax_kernel(const uint16_t* __res
     if (cur_g >= 0) flush();
 }
 
-template <int FMT, bool VEC, bool VEC_OUT, bool LDS>
+// ROWQ: also cast the tile along rows with the rowwise scales s_rows (already computed) and
+// write the row-major bytes q[r * ld_q + c] (the dual-layout call); ROWQ_VEC: 8-byte stores.
+template <int FMT, bool VEC, bool VEC_OUT, bool LDS, bool ROWQ = false, bool ROWQ_VEC = false>
 __global__ __launch_bounds__(256) void colwise_cast_kernel(
     const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ld_x,
     const int32_t* __restrict__ offsets, int G, const uint32_t* __restrict__ amax,
-    uint8_t* __restrict__ qt, int64_t ld_qt, float* __restrict__ scales) {
+    uint8_t* __restrict__ qt, int64_t ld_qt, float* __restrict__ scales,
+    const float* __restrict__ s_rows, uint8_t* __restrict__ q, int64_t ld_q) {
     const int t = threadIdx.x, o = t & 7, qd = t >> 3;
     const int64_t rb = (int64_t)blockIdx.x * CW_TR * CW_TPB_CAST, c0 = (int64_t)blockIdx.y * CW_TC;
     __shared__ __align__(16) float sc[CW_GB][CW_TC];
@@ -233,6 +253,27 @@ __global__ __launch_bounds__(256) void colwise_cast_kernel(
         if (r0 >= R) break;  // block-uniform
         if (k + 1 < CW_TPB_CAST) cw_load<VEC, true>(x, R, C, ld_x, r0 + CW_TR, c0, o, qd, vn);
         const int64_t r_end = r0 + CW_TR < R ? r0 + CW_TR : R;
+        if (ROWQ) {
+            // rowwise bytes of the lane's 8 rows x 8 columns, with each row's own scale
+            const int64_t c = c0 + 8 * o;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int64_t r = r0 + 8 * qd + i;
+                if (r >= R || c >= C) continue;
+                const float sr = s_rows[r] * Fmt<FMT>::mult;
+                const uint32_t lo = enc4<FMT>(cw_elem(v[i], 0) * sr, cw_elem(v[i], 1) * sr,
+                                              cw_elem(v[i], 2) * sr, cw_elem(v[i], 3) * sr);
+                const uint32_t hi = enc4<FMT>(cw_elem(v[i], 4) * sr, cw_elem(v[i], 5) * sr,
+                                              cw_elem(v[i], 6) * sr, cw_elem(v[i], 7) * sr);
+                uint8_t* dst = q + r * ld_q + c;
+                if (ROWQ_VEC) {
+                    *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+                } else {
+                    const uint32_t w[2] = {lo, hi};
+                    for (int j = 0; j < 8 && c + j < C; j++) dst[j] = (uint8_t)(w[j >> 2] >> (8 * (j & 3)));
+                }
+            }
+        }
         const int g_first = off.group_of(r0);
         const int g_last = off.group_of(r_end - 1);
         // group of each of the lane's rows (-1 past the end)
@@ -460,10 +501,10 @@ static void launch_cast(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x,
     const dim3 grid((unsigned)rt, (unsigned)ct);
     if (G <= CW_GLDS)
         colwise_cast_kernel<FMT, VEC, VEC_OUT, true><<<grid, dim3(256), 0, stream>>>(
-            x, R, C, ld_x, offsets, G, ws, qt, ld_qt, s);
+            x, R, C, ld_x, offsets, G, ws, qt, ld_qt, s, nullptr, nullptr, 0);
     else
         colwise_cast_kernel<FMT, VEC, VEC_OUT, false><<<grid, dim3(256), 0, stream>>>(
-            x, R, C, ld_x, offsets, G, ws, qt, ld_qt, s);
+            x, R, C, ld_x, offsets, G, ws, qt, ld_qt, s, nullptr, nullptr, 0);
 }
 
 // ------------------------------------------------------------------ weights in both layouts
@@ -616,17 +657,17 @@ static fp8q_status_t colwise_run(const uint16_t* x, int64_t R, int64_t C, int64_
         // cannot, and is read with streaming loads.
         const bool nt = (double)R * (double)ld_x * 2.0 > kStreamBytes;
         if (vec && lds && nt)
-            colwise_amax_kernel<true, true, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws);
+            colwise_amax_kernel<true, true, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws, nullptr);
         else if (vec && lds)
-            colwise_amax_kernel<true, true, false><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws);
+            colwise_amax_kernel<true, true, false><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws, nullptr);
         else if (vec && nt)
-            colwise_amax_kernel<true, false, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws);
+            colwise_amax_kernel<true, false, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws, nullptr);
         else if (vec)
-            colwise_amax_kernel<true, false, false><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws);
+            colwise_amax_kernel<true, false, false><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws, nullptr);
         else if (lds)
-            colwise_amax_kernel<false, true, false><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws);
+            colwise_amax_kernel<false, true, false><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws, nullptr);
         else
-            colwise_amax_kernel<false, false, false><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws);
+            colwise_amax_kernel<false, false, false><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws, nullptr);
     }
     if (vec && vec_out) launch_cast<FMT, true, true>(x, R, C, ld_x, offsets, G, ws, qt, ld_qt, s, stream);
     else if (vec) launch_cast<FMT, true, false>(x, R, C, ld_x, offsets, G, ws, qt, ld_qt, s, stream);
@@ -644,6 +685,136 @@ extern "C" size_t fp8_quant_colwise_grouped_workspace_size(int64_t rows, int64_t
     if (cols < 0 || groups < 1) return 0;
     const size_t b = (size_t)groups * (size_t)cols * sizeof(uint32_t);
     return (b + 255) & ~(size_t)255;
+}
+
+namespace fp8q {
+
+// ------------------------------------------------------------------ both layouts of activations
+// Rowwise scales from the per-(row, 64-column tile) maxima of the dual maxima pass.
+template <int FMT>
+__global__ __launch_bounds__(256) void dual_rowscale_kernel(const uint16_t* __restrict__ rowp,
+                                                            int64_t R, int nct,
+                                                            float* __restrict__ s_rows) {
+    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (r >= R) return;
+    const uint16_t* p = rowp + r * nct;
+    uint32_t m = 0;
+    for (int i = 0; i < nct; i++) m = max(m, (uint32_t)p[i]);
+    s_rows[r] = scale_from_amax<FMT>(__uint_as_float(m << 16));
+}
+
+// Workspace of the dual call: the (group, column) maxima, then the (row, column tile) maxima.
+static void dual_layout(int64_t R, int64_t C, int64_t G, size_t& o_rowp, size_t& total) {
+    const size_t a = ((size_t)G * (size_t)C * 4 + 255) & ~(size_t)255;
+    const size_t b = ((size_t)R * (size_t)((C + CW_TC - 1) / CW_TC) * 2 + 255) & ~(size_t)255;
+    o_rowp = a;
+    total = a + b;
+}
+
+template <int FMT, bool VEC, bool VEC_OUT, bool LDS>
+static void launch_cast_dual(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x,
+                             const int32_t* offsets, int G, const uint32_t* ws, uint8_t* qt,
+                             int64_t ld_qt, float* s, const float* s_rows, uint8_t* q,
+                             int64_t ld_q, bool rowq_vec, hipStream_t stream) {
+    const int64_t rt = R > 0 ? (R + CW_TR * CW_TPB_CAST - 1) / (CW_TR * CW_TPB_CAST) : 1;
+    const dim3 grid((unsigned)rt, (unsigned)((C + CW_TC - 1) / CW_TC));
+    if (rowq_vec)
+        colwise_cast_kernel<FMT, VEC, VEC_OUT, LDS, true, true><<<grid, dim3(256), 0, stream>>>(
+            x, R, C, ld_x, offsets, G, ws, qt, ld_qt, s, s_rows, q, ld_q);
+    else
+        colwise_cast_kernel<FMT, VEC, VEC_OUT, LDS, true, false><<<grid, dim3(256), 0, stream>>>(
+            x, R, C, ld_x, offsets, G, ws, qt, ld_qt, s, s_rows, q, ld_q);
+}
+
+template <int FMT>
+static fp8q_status_t dual_run(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x,
+                              const int32_t* offsets, int G, uint8_t* q, int64_t ld_q,
+                              float* s_rows, uint8_t* qt, int64_t ld_qt, float* s_cols,
+                              uint8_t* ws, hipStream_t stream) {
+    size_t o_rowp, total;
+    dual_layout(R, C, G, o_rowp, total);
+    uint32_t* amax = reinterpret_cast<uint32_t*>(ws);
+    uint16_t* rowp = reinterpret_cast<uint16_t*>(ws + o_rowp);
+    const bool vec = (C % 8 == 0) && (ld_x % 8 == 0) && fp8q_aligned(x, 16);
+    const bool vec_out = (ld_qt % 16 == 0) && fp8q_aligned(qt, 16);
+    const bool rowq_vec = (C % 8 == 0) && (ld_q % 8 == 0) && fp8q_aligned(q, 8);
+    const bool lds = G <= CW_GLDS;
+    const int64_t n = (int64_t)G * C;
+    int64_t zb = (n + 255) / 256;
+    if (zb > 4096) zb = 4096;
+    cw_zero_kernel<<<dim3((unsigned)zb), dim3(256), 0, stream>>>(amax, n);
+    if (R > 0) {
+        const dim3 grid((unsigned)((R + CW_TR * CW_TPB - 1) / (CW_TR * CW_TPB)),
+                        (unsigned)((C + CW_TC - 1) / CW_TC));
+        // the cast pass re-reads the input: streaming loads only past the last-level cache size
+        const bool nt = (double)R * (double)ld_x * 2.0 > kStreamBytes;
+        if (vec && lds && nt)
+            colwise_amax_kernel<true, true, true, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, amax, rowp);
+        else if (vec && lds)
+            colwise_amax_kernel<true, true, false, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, amax, rowp);
+        else if (vec && nt)
+            colwise_amax_kernel<true, false, true, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, amax, rowp);
+        else if (vec)
+            colwise_amax_kernel<true, false, false, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, amax, rowp);
+        else if (lds)
+            colwise_amax_kernel<false, true, false, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, amax, rowp);
+        else
+            colwise_amax_kernel<false, false, false, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, amax, rowp);
+        dual_rowscale_kernel<FMT><<<dim3((unsigned)((R + 255) / 256)), dim3(256), 0, stream>>>(
+            rowp, R, (int)grid.y, s_rows);
+    }
+    if (vec && vec_out && lds)
+        launch_cast_dual<FMT, true, true, true>(x, R, C, ld_x, offsets, G, amax, qt, ld_qt, s_cols, s_rows, q, ld_q, rowq_vec, stream);
+    else if (vec && vec_out)
+        launch_cast_dual<FMT, true, true, false>(x, R, C, ld_x, offsets, G, amax, qt, ld_qt, s_cols, s_rows, q, ld_q, rowq_vec, stream);
+    else if (vec && lds)
+        launch_cast_dual<FMT, true, false, true>(x, R, C, ld_x, offsets, G, amax, qt, ld_qt, s_cols, s_rows, q, ld_q, rowq_vec, stream);
+    else if (vec)
+        launch_cast_dual<FMT, true, false, false>(x, R, C, ld_x, offsets, G, amax, qt, ld_qt, s_cols, s_rows, q, ld_q, rowq_vec, stream);
+    else if (vec_out && lds)
+        launch_cast_dual<FMT, false, true, true>(x, R, C, ld_x, offsets, G, amax, qt, ld_qt, s_cols, s_rows, q, ld_q, rowq_vec, stream);
+    else if (vec_out)
+        launch_cast_dual<FMT, false, true, false>(x, R, C, ld_x, offsets, G, amax, qt, ld_qt, s_cols, s_rows, q, ld_q, rowq_vec, stream);
+    else if (lds)
+        launch_cast_dual<FMT, false, false, true>(x, R, C, ld_x, offsets, G, amax, qt, ld_qt, s_cols, s_rows, q, ld_q, rowq_vec, stream);
+    else
+        launch_cast_dual<FMT, false, false, false>(x, R, C, ld_x, offsets, G, amax, qt, ld_qt, s_cols, s_rows, q, ld_q, rowq_vec, stream);
+    FP8Q_CHECK_LAUNCH();
+    return FP8Q_OK;
+}
+
+}  // namespace fp8q
+
+extern "C" size_t fp8_quant_dual_grouped_workspace_size(int64_t rows, int64_t cols,
+                                                        int32_t groups) {
+    if (rows < 0 || cols < 0 || groups < 1) return 0;
+    size_t o, total;
+    fp8q::dual_layout(rows, cols, groups, o, total);
+    return total < 256 ? 256 : total;
+}
+
+extern "C" fp8q_status_t fp8_quant_dual_grouped(const uint16_t* x, int64_t rows, int64_t cols,
+                                                int64_t ld_x, const int32_t* offsets,
+                                                int32_t groups, fp8q_format_t fmt, uint8_t* q,
+                                                int64_t ld_q, float* s_rows, uint8_t* q_t,
+                                                int64_t ld_qt, float* s_cols, void* workspace,
+                                                size_t workspace_bytes, hipStream_t stream) {
+    if (rows < 0 || cols < 0 || groups < 1 || ld_x < cols || ld_q < cols || ld_qt < rows ||
+        !fp8q_fmt_ok(fmt) || !offsets)
+        return FP8Q_ERR_INVALID_ARG;
+    if (cols == 0) return FP8Q_OK;
+    if (!s_cols || (rows > 0 && (!x || !q || !s_rows || !q_t))) return FP8Q_ERR_INVALID_ARG;
+    if (workspace_bytes < fp8_quant_dual_grouped_workspace_size(rows, cols, groups) || !workspace)
+        return FP8Q_ERR_WORKSPACE;
+    if ((rows + fp8q::CW_TR - 1) / fp8q::CW_TR > 0x7FFFFFFFLL ||
+        (cols + fp8q::CW_TC - 1) / fp8q::CW_TC > 65535)
+        return FP8Q_ERR_UNSUPPORTED;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    if (fmt == FP8Q_E4M3FN)
+        return fp8q::dual_run<FP8Q_E4M3FN>(x, rows, cols, ld_x, offsets, groups, q, ld_q, s_rows,
+                                           q_t, ld_qt, s_cols, ws, stream);
+    return fp8q::dual_run<FP8Q_E4M3FNUZ>(x, rows, cols, ld_x, offsets, groups, q, ld_q, s_rows,
+                                         q_t, ld_qt, s_cols, ws, stream);
 }
 
 namespace fp8q {

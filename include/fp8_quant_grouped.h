@@ -137,6 +137,29 @@ fp8q_status_t fp8_quant_colwise_grouped(const uint16_t* x, int64_t rows, int64_t
                                         float* scales, void* workspace, size_t workspace_bytes,
                                         hipStream_t stream);
 
+/* Both layouts of an activation or gradient matrix in one call, for the operand that feeds one
+ * GEMM along rows and another along columns (activations: the forward and the weight gradient;
+ * gradients dY: the data gradient and the weight gradient).  Same results as the two separate
+ * calls, bit for bit:
+ *   q, s_rows   = fp8_quant_rowwise(x)                        (one scale per row)
+ *   q_t, s_cols = fp8_quant_colwise_grouped(x, offsets)       (one scale per (group, column))
+ * but x is read twice instead of three times: the maxima pass also records each row's maximum
+ * per 64-column tile, and the cast pass writes the row-major and the transposed bytes from the
+ * same loads (ai-radar.it, "Il guadagno vero e' nel movimento dei dati": every avoided pass
+ * over HBM counts).
+ *   x          bf16 [rows][ld_x]
+ *   offsets    int32 [groups] device (token groups, as for fp8_quant_colwise_grouped)
+ *   q          u8   [rows][ld_q], ld_q >= cols        s_rows fp32 [rows]
+ *   q_t        u8   [cols][ld_qt], ld_qt >= rows       s_cols fp32 [groups][cols]
+ *   workspace  >= fp8_quant_dual_grouped_workspace_size(rows, cols, groups) bytes, any content.
+ * Errors as for fp8_quant_colwise_grouped.  cols == 0 is a no-op. */
+size_t fp8_quant_dual_grouped_workspace_size(int64_t rows, int64_t cols, int32_t groups);
+fp8q_status_t fp8_quant_dual_grouped(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                     const int32_t* offsets, int32_t groups, fp8q_format_t fmt,
+                                     uint8_t* q, int64_t ld_q, float* s_rows, uint8_t* q_t,
+                                     int64_t ld_qt, float* s_cols, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+
 /* fp8_quant_colwise_grouped without a workspace argument and without any allocation, for
  * callers that cannot allocate device memory: code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc.  Same arguments (minus the workspace), results and

@@ -109,6 +109,26 @@ def test_colwise_full_dsv3_wgrad_operands(fq, dsv3_bwd, which):
     assert np.array_equal(buf[:, :M].cpu().numpy(), oqt)
 
 
+@pytest.mark.parametrize("which", ["x", "dy"])
+def test_dual_full_dsv3(fq, dsv3_bwd, which):
+    """Both layouts of the dsv3 activations X [16384, 7168] and gradients dY [16384, 2048] in one
+    call (the padded transposed buffers the weight gradient reads), every byte and scale."""
+    d = dsv3_bwd
+    a = d[which]
+    M = d["M"]
+    ldm = -(-M // 16) * 16
+    buf = torch.empty((a.shape[1], ldm), dtype=torch.uint8, device=DEV)
+    (q, sr), (qt, sc) = fq.fp8_quant_dual_grouped(workloads.to_torch_bf16(a, DEV),
+                                                  dev(d["offsets"]), FN, q_t=buf[:, :M])
+    oq, os_ = oracle.quant_rowwise(a, FN)
+    assert np.array_equal(sr.cpu().numpy(), os_)
+    assert np.array_equal(q.cpu().numpy(), oq)
+    del q, oq
+    oqt, osc = oracle.quant_colwise_grouped(a, d["offsets"], FN)
+    assert np.array_equal(sc.cpu().numpy(), osc)
+    assert np.array_equal(buf[:, :M].cpu().numpy(), oqt)
+
+
 def test_mx_quant_full_dsv3(fq, dsv3_fwd):
     d = dsv3_fwd
     q, e = fq.fp8_mx_quant_rowwise(workloads.to_torch_bf16(d["x"], DEV))

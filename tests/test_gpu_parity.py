@@ -709,3 +709,39 @@ def test_gemm_fwd_stale_lds_rows_never_reach_stored_rows(fq):
     assert np.all(np.isfinite(got))
     mm.check_gemm(got, ref, "fwd after NaN tiles",
                   mm.explain_fwd(FN, qa, sa, qbt, E * K, K, sb, off, N, K, rows=rows))
+
+
+# ----------------------------------------------------------------------------- both layouts
+
+DUAL_CASES = [
+    # rows, cols, offsets, ld pad of x, ld pad of q
+    (1024, 256, [485, 524, 774, 1024], 0, 0),           # the C1 activation shapes
+    (513, 130, [0, 37, 37, 256, 256, 257, 512, 513], 8, 0),  # ragged tiles, empty groups
+    (700, 72, [100, 100, 356, 612, 700, 700], 0, 5),    # byte-wise rowwise stores (ld_q % 8)
+    (259, 21, [3, 259], 0, 0),                          # columns not a multiple of 8
+    (4300, 24, sorted(np.random.Generator(np.random.PCG64(12)).integers(0, 4301, 2099).tolist())
+     + [4300], 0, 0),                                    # groups beyond the LDS offsets copy
+    (3000, 7168, [150, 900, 901, 2999, 3000], 0, 0),     # the DeepSeek-V3 hidden width
+]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("case", DUAL_CASES)
+def test_dual_layout_parity(fq, fmt, case):
+    """fp8_quant_dual_grouped: the rowwise bytes and scales equal the oracle's rowwise
+    quantization and the transposed ones its colwise grouped quantization, bit for bit, with
+    nothing written past either output's rows."""
+    rows, cols, off, padx, padq = case
+    x = workloads.make_matrix(1300 + rows + cols, rows, cols, 1.0, 0.01)
+    off = np.asarray(off, np.int32)
+    qbuf = torch.full((rows, cols + padq), 0xCD, dtype=torch.uint8, device=DEV)
+    (q, sr), (qt, sc) = fq.fp8_quant_dual_grouped(dev_bf16(x, ld=cols + padx if padx else None),
+                                                  dev_i32(off), fmt, q=qbuf[:, :cols])
+    oq, os_ = oracle.quant_rowwise(x, fmt)
+    oqt, osc = oracle.quant_colwise_grouped(x, off, fmt)
+    qb = qbuf.cpu().numpy()
+    assert np.array_equal(sr.cpu().numpy(), os_)
+    assert np.array_equal(qb[:, :cols], oq)
+    assert np.all(qb[:, cols:] == 0xCD)
+    assert np.array_equal(sc.cpu().numpy(), osc)
+    assert np.array_equal(qt.cpu().numpy(), oqt)
