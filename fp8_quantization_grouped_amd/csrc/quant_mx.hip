@@ -61,6 +61,7 @@ __global__ __launch_bounds__(256) void mx_rowwise_kernel(const uint16_t* __restr
 // with consecutive row octets (lane bits 3-4) form a 32-row block; bytes are encoded along rows,
 // transposed through LDS and written as 16-byte chunks of the column-major output.
 constexpr int MXC_TR = 256, MXC_TC = 64, MXC_STR = MXC_TR + 16;
+// (transposed tile layout with the column-octet XOR swizzle of quant_colwise.hip's tiles)
 
 __global__ __launch_bounds__(256) void mx_colwise_kernel(const uint16_t* __restrict__ x,
                                                          int64_t R, int64_t C, int64_t ld_x,
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(256) void mx_colwise_kernel(const uint16_t* __restr
         }
         const uint32_t w0 = enc4<FP8Q_E4M3FN>(y[0], y[1], y[2], y[3]);
         const uint32_t w1 = enc4<FP8Q_E4M3FN>(y[4], y[5], y[6], y[7]);
-        *reinterpret_cast<uint2*>(&tile[(8 * o + j) * MXC_STR + 8 * qd]) = make_uint2(w0, w1);
+        *reinterpret_cast<uint2*>(&tile[(8 * o + j) * MXC_STR + 8 * (qd ^ (2 * o))]) = make_uint2(w0, w1);
     }
     __syncthreads();
 #pragma unroll
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(256) void mx_colwise_kernel(const uint16_t* __restr
         const int col = ch >> 4, seg = ch & 15;
         const int64_t cc = c0 + col, r = r0 + 16 * seg;
         if (cc >= C || r >= R) continue;
-        const uint8_t* src = &tile[col * MXC_STR + 16 * seg];
+        const uint8_t* src = &tile[col * MXC_STR + 16 * (seg ^ ((col >> 3) & 7))];
         uint8_t* dst = qt + cc * ld_qt + r;
         if (vec_out && r + 16 <= R) {
             if (nt_out) st_nt16(dst, *reinterpret_cast<const uint4*>(src));  // block-uniform
