@@ -466,10 +466,14 @@ __global__ __launch_bounds__(TR) void colwise_long_kernel(
     const float4 sa = *reinterpret_cast<const float4*>(&scl[8 * o]);
     const float4 sb = *reinterpret_cast<const float4*>(&scl[8 * o + 4]);
     const float sj[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
-    // pass 2: cast, transpose through LDS, write 16-byte chunks of each column's run
+    // pass 2: cast, transpose through LDS, write 16-byte chunks of each column's run; the next
+    // tile's loads are issued before this tile's transpose and stores
+    uint4 v[8];
+    if (tb < ge) load(tb, v, true);
     for (int64_t r0 = tb; r0 < ge; r0 += CL_TR) {
-        uint4 v[8];
-        load(r0, v, true);
+        uint4 vn[8];
+        const bool more = r0 + CL_TR < ge;  // block-uniform
+        if (more) load(r0 + CL_TR, vn, true);
         __syncthreads();  // the previous tile's bytes have been stored
 #pragma unroll
         for (int j = 0; j < 8; j++) {
@@ -494,6 +498,10 @@ __global__ __launch_bounds__(TR) void colwise_long_kernel(
                 for (int bb = 0; bb < 16; bb++)
                     if (r + bb >= gs && r + bb < ge) dst[bb] = src[bb];
             }
+        }
+        if (more) {
+#pragma unroll
+            for (int i = 0; i < 8; i++) v[i] = vn[i];
         }
     }
 }
