@@ -199,16 +199,15 @@ struct Tile {  // all extents < 2^31 (checked on the host)
     int row_lo, row_hi, n0, kb_lo, kb_hi, kstart, nk, a_rows, b_rows;
 };
 
-// One block per CU runs a contiguous range of the tile sequence (persistent schedule).
-// Forward: tiles ordered by group, then column tile, then row tile (fastest), every tile the
-// same work, so a group's row tiles that share a weight tile run together; weight gradient: tiles ordered by group, each weighted by its contraction steps
-// plus one for its epilogue, so the ranges split the real work evenly whatever the group
-// sizes.  Ranges of one XCD are adjacent (blocks are dealt to XCDs round-robin), so concurrent
-// tiles share operand tiles in that XCD's L2.  The first contraction step of a block's next
-// tile is fetched while the current tile finishes.
-// MX scale loading: none (plain FP8), per-step byte loads (any scale strides), or one 16-byte
-// DMA per row and side every 4 contraction steps (16-byte aligned scale rows).
-constexpr int MX_NONE = 0, MX_BYTES = 1, MX_DMA = 2;
+// One block per CU runs its share of the tile sequence (persistent schedule; see the schedule
+// comments in the kernel).  The first contraction step of a block's next tile is fetched while
+// the current tile finishes.
+// MX scale loading: none (plain FP8); per-step byte loads into registers (any scale strides);
+// one 16-byte DMA per row and side every 4 contraction steps (16-byte aligned scale rows, the
+// forward); or one dword DMA per row and side per step (MX_DW: 4-byte aligned scale rows, the
+// weight gradient, whose tiles then start on 128-token boundaries so that a step's 4 scale
+// bytes are one aligned dword).
+constexpr int MX_NONE = 0, MX_BYTES = 1, MX_DMA = 2, MX_DW = 3;
 
 template <int FMT, int MODE, int MXV, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
@@ -220,8 +219,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
     // chunks instead (its tiles are long, so the per-tile offsets loads do not matter there)
     constexpr bool OFF_LDS = MXV != MX_DMA;
     __shared__ __align__(16) uint8_t smem[2][2][STAGE];
-    // MX_BYTES: 4 E8M0 bytes per row and step (by stage); otherwise the fp32 dequant scales of
-    // the tile's rows [0] and columns [1] (by tile parity)
+    // MX_BYTES, MX_DW: 4 E8M0 bytes per row and step (by stage); otherwise the fp32 dequant
+    // scales of the tile's rows [0] and columns [1] (by tile parity)
     __shared__ __align__(16) uint32_t sscale[2][2][GT];
     // MX_DMA: E8M0 bytes of 4 steps (16 K blocks) per row: [slot][side][row][16]
     __shared__ __align__(16) uint8_t smx[MXV == MX_DMA ? 2 * 2 * GT * 16 : 16];
@@ -245,7 +244,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
     const int64_t tiles_per_group = (int64_t)p.nt_k * p.nt_n;
     // weight gradient: a tile's contraction starts at its group's first token rounded down to
     // 16 (one LDS chunk), or to 32 for MX so that the steps' 32-token blocks are the scale blocks
-    constexpr int64_t KALIGN = MX ? 31 : 15;
+    // (128 with dword scale DMA: a step's four scale bytes are then one aligned dword)
+    constexpr int64_t KALIGN = MXV == MX_DW ? 127 : MX ? 31 : 15;
 
     if (OFF_LDS) {
         for (int i = t; i < p.G; i += NT) s_off[i] = p.offsets[i];
@@ -507,6 +507,20 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
             dma16(rsa, oa, lds_addr(&smx[((slot * 2 + 0) * GT + wave * 64) * 16]));
             dma16(rsb, ob, lds_addr(&smx[((slot * 2 + 1) * GT + wave * 64) * 16]));
         }
+        if (MXV == MX_DW && row_thread) {
+            // rows t of both tiles: the 4 E8M0 bytes of this step (kpos is a multiple of 128, so
+            // they are one aligned dword) straight into the stage's scale rows.  Blocks past
+            // the group's end are replaced by 2^0 where they are read.
+            const i32x4_t rsa =
+                make_rsrc4(p.a_e8 + (int64_t)T.row_lo * p.ld_sa, (uint32_t)(T.a_rows * p.ld_sa));
+            const i32x4_t rsb = make_rsrc4(p.b_e8 + (int64_t)T.g * p.sbgs + (int64_t)T.n0 * p.ld_sb,
+                                           (uint32_t)(T.b_rows * p.ld_sb));
+            const uint32_t kb0 = (uint32_t)(kpos / 32);
+            const uint32_t oa = t < T.a_rows ? (uint32_t)t * (uint32_t)p.ld_sa + kb0 : OOB;
+            const uint32_t ob = t < T.b_rows ? (uint32_t)t * (uint32_t)p.ld_sb + kb0 : OOB;
+            dma4(rsa, oa, lds_addr(&sscale[stage][0][(wave & 3) * 64]));
+            dma4(rsb, ob, lds_addr(&sscale[stage][1][(wave & 3) * 64]));
+        }
         if (MXV == MX_BYTES && row_thread) {
             // rows t of both tiles: the 4 E8M0 bytes of this 128-byte step, packed into one
             // dword per row (blocks past K get 127 = 2^0: their data bytes are zero)
@@ -620,15 +634,19 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
                 // threads 0-255 take the rows of the activation tile, 256-511 those of the
                 // gradient tile (at least 8 waves: wave-uniform sides)
                 static_assert(NW >= 8, "two tile sides over 512 threads");
-                if (t < 2 * GT) {
-                    const int zr = t & (GT - 1);
-                    uint8_t* side = smem[cur_st][t >> 8];
+                // an opaque copy of the thread id: the addresses below are recomputed here
+                // instead of being held in registers across the whole tile
+                int tt = t;
+                asm volatile("" : "+v"(tt));
+                if (tt < 2 * GT) {
+                    const int zr = tt & (GT - 1);
+                    uint8_t* side = smem[cur_st][tt >> 8];
 #pragma unroll
                     for (int ch = 0; ch < 8; ch++) {
                         const int b0 = 16 * ch;
                         if ((lo > b0 && lo < b0 + 16) || (hi > b0 && hi < b0 + 16)) {
                             uint4* q = reinterpret_cast<uint4*>(
-                                side + (t < GT ? lds_off(zr, ch) : lds_offB(zr, ch)));
+                                side + (tt < GT ? lds_off(zr, ch) : lds_offB(zr, ch)));
                             uint4 w = *q;
                             w.x &= keep_mask4(lo, hi, b0);
                             w.y &= keep_mask4(lo, hi, b0 + 4);
@@ -680,7 +698,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
                 // scale bytes are read unconditionally (in-range LDS) and then selected: a
                 // conditional read becomes a branch per row, and the compiler then gathers all
                 // fragment reads ahead of the matrix instructions (registers spill)
-                if (MXV == MX_BYTES) {
+                if (MXV == MX_BYTES || MXV == MX_DW) {
                     const int e = (int)((sscale[cur_st][1][rn] >> (8 * kg)) & 0xFFu);
                     sb_[j] = kb_in ? e : 127;
                 }
@@ -706,7 +724,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
                 }
                 if (pend && MX && NW == 4 && i < NP) part(P, i);  // 4-wave MX: one part per row
                 int sa_ = 0;
-                if (MXV == MX_BYTES) {
+                if (MXV == MX_BYTES || MXV == MX_DW) {
                     const int e = (int)((sscale[cur_st][0][ma_byt + 16 * i] >> (8 * kg)) & 0xFFu);
                     sa_ = kb_in ? e : 127;
                 }
@@ -975,7 +993,11 @@ extern "C" fp8q_status_t fp8_mx_grouped_gemm_wgrad(const uint8_t* a, int64_t lda
     p.bgs = 0; p.b_e8 = b_e8m0; p.ld_sb = ld_sb; p.sbgs = 0;
     p.offsets = offsets; p.G = groups; p.M = M; p.N = N; p.K = K;
     p.c = reinterpret_cast<uint8_t*>(c); p.ldc = ldc;
-    // per-step byte loads of the scales: a tile's first 32-token block need not be 16-aligned
+    // scale rows 4-byte aligned: one dword of scales per row, side and step by DMA, tiles
+    // starting on 128-token boundaries; otherwise per-step byte loads of the scales
+    const bool dw = ld_sa % 4 == 0 && ld_sb % 4 == 0 && fp8q_aligned(a_e8m0, 4) &&
+                    fp8q_aligned(b_e8m0, 4);
+    if (dw) return launch_gemm<FP8Q_E4M3FN, MODE_WGRAD, MX_DW>(p, stream);
     return launch_gemm<FP8Q_E4M3FN, MODE_WGRAD, MX_BYTES>(p, stream);
 }
 
