@@ -130,7 +130,8 @@ __global__ void cw_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
 }
 
 // ROWP: also write each row's maximum over the tile's 64 columns (bf16 magnitude bits) to
-// rowp[r * gridDim.y + blockIdx.y]: the dual-layout call reduces them into rowwise scales.
+// rowp[blockIdx.y * Rp + r] (Rp = R rounded up to 8; each lane of a row group stores its 8
+// consecutive rows at once): the dual-layout call reduces them into rowwise scales.
 template <bool VEC, bool LDS, bool NT, bool ROWP = false>
 __global__ __launch_bounds__(256) void colwise_amax_kernel(const uint16_t* __restrict__ x,
                                                            int64_t R, int64_t C, int64_t ld_x,
@@ -180,7 +181,9 @@ __global__ __launch_bounds__(256) void colwise_amax_kernel(const uint16_t* __res
         if (k + 1 < CW_TPB) cw_load<VEC, NT>(x, R, C, ld_x, r0 + CW_TR, c0, o, qd, vn);
         const int64_t r_end = r0 + CW_TR < R ? r0 + CW_TR : R;
         if (ROWP) {
-            // the 8 lanes of a row group (o = 0..7, consecutive lanes) hold its 64 columns
+            // the 8 lanes of a row group (o = 0..7, consecutive lanes) hold its 64 columns;
+            // lane o = 0 stores the maxima of its 8 rows as one 16-byte piece
+            uint32_t pk[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
             for (int i = 0; i < 8; i++) {
                 uint32_t m = pk_max_u16(pk_max_u16(mag2(v[i].x), mag2(v[i].y)),
@@ -189,9 +192,12 @@ __global__ __launch_bounds__(256) void colwise_amax_kernel(const uint16_t* __res
                 m = max(m, (uint32_t)__shfl_xor((int)m, 1, 64));
                 m = max(m, (uint32_t)__shfl_xor((int)m, 2, 64));
                 m = max(m, (uint32_t)__shfl_xor((int)m, 4, 64));
-                const int64_t r = r0 + 8 * qd + i;
-                if (o == 0 && r < R) rowp[r * (int64_t)gridDim.y + blockIdx.y] = (uint16_t)m;
+                pk[i >> 1] |= m << (16 * (i & 1));
             }
+            const int64_t Rp = (R + 7) & ~(int64_t)7, r = r0 + 8 * qd;
+            if (o == 0 && r < Rp)
+                *reinterpret_cast<uint4*>(rowp + (int64_t)blockIdx.y * Rp + r) =
+                    make_uint4(pk[0], pk[1], pk[2], pk[3]);
         }
         const int g_first = off.group_of(r0);
         const int g_last = off.group_of(r_end - 1);
@@ -709,18 +715,27 @@ template <int FMT>
 __global__ __launch_bounds__(256) void dual_rowscale_kernel(const uint16_t* __restrict__ rowp,
                                                             int64_t R, int nct,
                                                             float* __restrict__ s_rows) {
-    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (r >= R) return;
-    const uint16_t* p = rowp + r * nct;
+    // 64 rows per block, each reduced by 4 threads (one per wave) over every 4th column tile:
+    // the loads of a wave cover 64 consecutive rows of one column tile
+    __shared__ uint32_t red[4][64];
+    const int t = threadIdx.x, part = t >> 6;
+    const int64_t Rp = (R + 7) & ~(int64_t)7, r = (int64_t)blockIdx.x * 64 + (t & 63);
     uint32_t m = 0;
-    for (int i = 0; i < nct; i++) m = max(m, (uint32_t)p[i]);
-    s_rows[r] = scale_from_amax<FMT>(__uint_as_float(m << 16));
+    if (r < R)
+        for (int i = part; i < nct; i += 4) m = max(m, (uint32_t)rowp[(int64_t)i * Rp + r]);
+    red[part][t & 63] = m;
+    __syncthreads();
+    if (t < 64 && r < R) {
+        const uint32_t mm = max(max(red[0][t], red[1][t]), max(red[2][t], red[3][t]));
+        s_rows[r] = scale_from_amax<FMT>(__uint_as_float(mm << 16));
+    }
 }
 
-// Workspace of the dual call: the (group, column) maxima, then the (row, column tile) maxima.
+// Workspace of the dual call: the (group, column) maxima, then the (column tile, row) maxima.
 static void dual_layout(int64_t R, int64_t C, int64_t G, size_t& o_rowp, size_t& total) {
     const size_t a = ((size_t)G * (size_t)C * 4 + 255) & ~(size_t)255;
-    const size_t b = ((size_t)R * (size_t)((C + CW_TC - 1) / CW_TC) * 2 + 255) & ~(size_t)255;
+    const size_t Rp = ((size_t)R + 7) & ~(size_t)7;  // rows of each column tile, padded to 8
+    const size_t b = (Rp * (size_t)((C + CW_TC - 1) / CW_TC) * 2 + 255) & ~(size_t)255;
     o_rowp = a;
     total = a + b;
 }
@@ -774,7 +789,7 @@ static fp8q_status_t dual_run(const uint16_t* x, int64_t R, int64_t C, int64_t l
             colwise_amax_kernel<false, true, false, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, amax, rowp);
         else
             colwise_amax_kernel<false, false, false, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, amax, rowp);
-        dual_rowscale_kernel<FMT><<<dim3((unsigned)((R + 255) / 256)), dim3(256), 0, stream>>>(
+        dual_rowscale_kernel<FMT><<<dim3((unsigned)((R + 63) / 64)), dim3(256), 0, stream>>>(
             rowp, R, (int)grid.y, s_rows);
     }
     if (vec && vec_out && lds)
@@ -820,6 +835,7 @@ extern "C" fp8q_status_t fp8_quant_dual_grouped(const uint16_t* x, int64_t rows,
     if (!s_cols || (rows > 0 && (!x || !q || !s_rows || !q_t))) return FP8Q_ERR_INVALID_ARG;
     if (workspace_bytes < fp8_quant_dual_grouped_workspace_size(rows, cols, groups) || !workspace)
         return FP8Q_ERR_WORKSPACE;
+    if (!fp8q_aligned(workspace, 16)) return FP8Q_ERR_INVALID_ARG;  // 16-byte row-maxima stores
     if ((rows + fp8q::CW_TR - 1) / fp8q::CW_TR > 0x7FFFFFFFLL ||
         (cols + fp8q::CW_TC - 1) / fp8q::CW_TC > 65535)
         return FP8Q_ERR_UNSUPPORTED;

@@ -151,7 +151,8 @@ fp8q_status_t fp8_quant_colwise_grouped(const uint16_t* x, int64_t rows, int64_t
  *   offsets    int32 [groups] device (token groups, as for fp8_quant_colwise_grouped)
  *   q          u8   [rows][ld_q], ld_q >= cols        s_rows fp32 [rows]
  *   q_t        u8   [cols][ld_qt], ld_qt >= rows       s_cols fp32 [groups][cols]
- *   workspace  >= fp8_quant_dual_grouped_workspace_size(rows, cols, groups) bytes, any content.
+ *   workspace  >= fp8_quant_dual_grouped_workspace_size(rows, cols, groups) bytes, any content,
+ *              16-byte aligned (FP8Q_ERR_INVALID_ARG otherwise).
  * Errors as for fp8_quant_colwise_grouped.  cols == 0 is a no-op. */
 size_t fp8_quant_dual_grouped_workspace_size(int64_t rows, int64_t cols, int32_t groups);
 fp8q_status_t fp8_quant_dual_grouped(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
