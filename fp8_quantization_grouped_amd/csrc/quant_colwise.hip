@@ -260,6 +260,16 @@ __global__ __launch_bounds__(256) void colwise_cast_kernel(
     int sc_lo = -1, sc_hi = -2;  // groups held in sc (block-uniform)
     uint4 v[8], vn[8];
     cw_load<VEC, true>(x, R, C, ld_x, rb, c0, o, qd, v);
+    // ROWQ: the rowwise scales of the lane's 8 rows, loaded with the tile (one tile per block)
+    static_assert(!ROWQ || CW_TPB_CAST == 1, "row scales are loaded for the block's one tile");
+    float srow[8];
+    if (ROWQ) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int64_t r = rb + 8 * qd + i;
+            srow[i] = r < R ? s_rows[r] * Fmt<FMT>::mult : 0.0f;
+        }
+    }
     for (int k = 0; k < CW_TPB_CAST; k++) {
         const int64_t r0 = rb + (int64_t)k * CW_TR;
         if (r0 >= R) break;  // block-uniform
@@ -272,7 +282,7 @@ __global__ __launch_bounds__(256) void colwise_cast_kernel(
             for (int i = 0; i < 8; i++) {
                 const int64_t r = r0 + 8 * qd + i;
                 if (r >= R || c >= C) continue;
-                const float sr = s_rows[r] * Fmt<FMT>::mult;
+                const float sr = srow[i];
                 const uint32_t lo = enc4<FMT>(cw_elem(v[i], 0) * sr, cw_elem(v[i], 1) * sr,
                                               cw_elem(v[i], 2) * sr, cw_elem(v[i], 3) * sr);
                 const uint32_t hi = enc4<FMT>(cw_elem(v[i], 4) * sr, cw_elem(v[i], 5) * sr,
