@@ -2,10 +2,15 @@
 
 One step = one pass of every hot-path operation over one batch of synthetic input resident in
 HBM:
-  forward   rowwise quant of X, per-expert colwise quant of W (transposed), M-grouped FP8 GEMM
-  backward  colwise-grouped transposed quant of X and dY, K-grouped FP8 weight-gradient GEMM
+  X         both FP8 layouts of X in one call: rowwise (the forward's A operand) and the
+            token-grouped transposed colwise copy (the weight gradient's A operand)
+  forward   per-expert colwise quant of W (transposed), M-grouped FP8 GEMM
+  backward  colwise-grouped transposed quant of dY, K-grouped FP8 weight-gradient GEMM
   MXFP8     MX rowwise quant of X, MX colwise quant of W, MX grouped GEMM (forward)
+  (a configuration without the backward quantizes X rowwise only)
 Next rows, timed in passes of their own after the step and reported under "next_rows":
+  the two single-layout quantizations of X (rowwise, transposed colwise) that the dual call
+  replaces, and both layouts of dY in one call;
   rowwise quant of routed rows gathered in expert order from 2048 token rows (top-8);
   rowwise quant of dY and of W along N, M-grouped FP8 data-gradient GEMM (dX = dY W^T);
   MX colwise quant of X and dY along tokens, MX K-grouped weight-gradient GEMM.
@@ -141,7 +146,8 @@ class Step:
                 ws_dy=e(max(256, fq.fp8_quant_colwise_grouped_workspace_size(M, N, G))),
                 # both layouts of X and of dY in one call each (rowwise + transposed)
                 dxq=e(M, K), dxs=e(M, dt=f32), dyq2=e(M, N), dys2=e(M, dt=f32),
-                ws_dual=e(max(256, fq.fp8_quant_dual_grouped_workspace_size(M, K, G))))
+                ws_dual=e(max(256, fq.fp8_quant_dual_grouped_workspace_size(M, K, G),
+                                      fq.fp8_quant_dual_grouped_workspace_size(M, N, G))))
         if "gather" in d["ops"]:
             # dispatch in expert order: 2048 tokens x top-8 over 32 experts (seeded Zipf routing)
             import workloads
@@ -156,7 +162,7 @@ class Step:
             # both weight layouts in one call (quantized once per optimizer step)
             self.buf.update(dwr=e(E * K, N), dwrs=e(E * K, dt=f32), dwt=e(N, E * K),
                             dwts=e(E, N, dt=f32),
-                            ws_dual=e(max(256, fq.fp8_quant_weights_dual_workspace_size(E, K, N))))
+                            ws_wdual=e(max(256, fq.fp8_quant_weights_dual_workspace_size(E, K, N))))
         if "mx" in d["ops"]:
             self.buf.update(mxq=e(M, K), mxe=e(M, K // 32), mxwt=e(N, E * K),
                             mxwe=e(N, E * K // 32), ymx=e(M, N, dt=bf))
@@ -209,9 +215,15 @@ class Step:
     def ops(self):
         fq, d, b = self.fq, self.d, self.buf
         M, K, N, E, fmt = d["M"], d["K"], d["N"], d["E"], d["fmt"]
+        q_rows_x = ("quant_rowwise_x", lambda: fq.fp8_quant_rowwise(d["x"], fmt, q=b["xq"],
+                                                                    scales=b["sx"]))
+        # with the backward in the step, X's two layouts come from one call (bit-identical to
+        # the rowwise and the transposed colwise calls, which are timed among the next rows)
+        dual_x = ("quant_dual_x", lambda: fq.fp8_quant_dual_grouped(
+            d["x"], d["offsets"], fmt, q=b["xq"], s_rows=b["sx"], q_t=b["xqt"][:, :M],
+            s_cols=b["sxg"], workspace=b["ws_dual"]))
         seq = [
-            ("quant_rowwise_x", lambda: fq.fp8_quant_rowwise(d["x"], fmt, q=b["xq"],
-                                                             scales=b["sx"])),
+            dual_x if "wgrad" in d["ops"] else q_rows_x,
             ("quant_colwise_w", lambda: fq.fp8_quant_colwise_grouped(
                 d["w"], self.off_w, fmt, q_t=b["wqt"], scales=b["sw"].view(E, N),
                 workspace=b["ws_w"])),
@@ -227,9 +239,6 @@ class Step:
                 d["x"][: M // 8], self.gidx, fmt, q=b["gq"], scales=b["gs"]))]
         if "wgrad" in d["ops"]:
             seq += [
-                ("quant_colwise_xT", lambda: fq.fp8_quant_colwise_grouped(
-                    d["x"], d["offsets"], fmt, q_t=b["xqt"][:, :M], scales=b["sxg"],
-                    workspace=b["ws_x"])),
                 ("quant_colwise_dyT", lambda: fq.fp8_quant_colwise_grouped(
                     d["dy"], d["offsets"], fmt, q_t=b["dyqt"][:, :M], scales=b["sdyg"],
                     workspace=b["ws_dy"])),
@@ -238,12 +247,13 @@ class Step:
                     d["offsets"], M, N, K, ldb=self.ldm, c=b["dw"], workspace=b["gws"])),
             ]
         if "wgrad" in d["ops"]:
-            # both layouts at once: X for the forward and the weight gradient, dY for the data
-            # gradient and the weight gradient (compare with the rowwise + transposed calls)
+            # X's single-layout calls (the step uses the dual call); both layouts of dY at once,
+            # for the data gradient and the weight gradient
             extra += [
-                ("quant_dual_x", lambda: fq.fp8_quant_dual_grouped(
-                    d["x"], d["offsets"], fmt, q=b["dxq"], s_rows=b["dxs"], q_t=b["xqt"][:, :M],
-                    s_cols=b["sxg"], workspace=b["ws_dual"])),
+                q_rows_x,
+                ("quant_colwise_xT", lambda: fq.fp8_quant_colwise_grouped(
+                    d["x"], d["offsets"], fmt, q_t=b["xqt"][:, :M], scales=b["sxg"],
+                    workspace=b["ws_x"])),
                 ("quant_dual_dy", lambda: fq.fp8_quant_dual_grouped(
                     d["dy"], d["offsets"], fmt, q=b["dyq2"], s_rows=b["dys2"],
                     q_t=b["dyqt"][:, :M], s_cols=b["sdyg"], workspace=b["ws_dual"])),
@@ -262,7 +272,7 @@ class Step:
                     workspace=b["gws"])),
                 ("quant_weights_dual", lambda: fq.fp8_quant_weights_dual(
                     d["w"], E, fmt, q_rows=b["dwr"], s_rows=b["dwrs"], q_t=b["dwt"],
-                    s_cols=b["dwts"], workspace=b["ws_dual"])),
+                    s_cols=b["dwts"], workspace=b["ws_wdual"])),
             ]
         if "mx" in d["ops"]:
             seq += [
