@@ -374,8 +374,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
     auto tile_start = [&](Tile& T) -> bool {
         if (MODE == MODE_FWD) {
             if (ti >= t_end) return false;
-            // tiles of one group are ordered (column tile, row tile), row tile fastest, so the
-            // row tiles sharing a weight tile run side by side in one XCD
+            // the row tiles sharing a weight tile run side by side in one XCD
             int lo = 0, hi = p.G - 1;  // last group whose tiles start at or before ti
             while (lo < hi) {
                 const int mid = (lo + hi + 1) >> 1;
@@ -384,8 +383,15 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm256_kernel(const GemmArgs p) {
             T.g = lo;
             const int rt = s_pref[lo + 1] - s_pref[lo];  // row tiles of the group (> 0 here)
             const int l = ti - s_pref[lo] * p.nt_n;
-            T.n0 = (l / rt) * GT;
-            T.row_lo = (l % rt) * GT;  // relative to the group start
+            // bands of up to 8 row tiles, each band ordered (column tile, row tile) with the row
+            // tile fastest: an XCD's 32 concurrent tiles cover 4 columns x 8 rows of a large
+            // group (12 distinct operand tiles instead of up to 33 for one column of row tiles;
+            // dense 8192 x 4096 x 14336: 493 -> 448 us)
+            constexpr int BAND = 8;
+            const int bt = BAND * p.nt_n, b = l / bt, r = l - b * bt;
+            const int rows_b = rt - b * BAND < BAND ? rt - b * BAND : BAND;
+            T.n0 = (r / rows_b) * GT;
+            T.row_lo = (b * BAND + r % rows_b) * GT;  // relative to the group start
             ti += bpx;
         } else {
             // round r takes tiles [r*nb, r*nb + nb) of the size order; XCD x (blocks are dealt
