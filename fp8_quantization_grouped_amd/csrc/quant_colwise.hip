@@ -11,8 +11,8 @@
 //
 // gfx950 design.  A column's absmax needs every row of its group before any element can be
 // cast, and a group can span thousands of rows, so the work is two passes over 256x64 tiles:
-//   1. colwise_amax_kernel: each block walks 4 consecutive 256-row x 64-column tiles (8 rows x
-//      8 columns per lane, 16-byte loads, 128 contiguous bytes per row, the next tile's loads
+//   1. colwise_amax_kernel: each block walks 1, 2 or 4 consecutive 256-row x 64-column tiles
+//      (8 rows x 8 columns per lane, 16-byte loads, 128 contiguous bytes per row, the next tile's loads
 //      in flight while the current one is reduced), keeps per-lane column maxima of the group
 //      it is in (packed 16-bit max on bf16 magnitude bits), and when the group changes reduces
 //      them to 64 column maxima (lane shuffles, then LDS across the 4 waves) and publishes them
@@ -45,7 +45,6 @@ constexpr int CW_STR = CW_TR + 16;      // LDS bytes per transposed column (16-b
 // for each half-wave (8 cycles per write instead of 2; rocprof counted 64-80% of these kernels'
 // LDS cycles as bank conflicts).  The reads stay conflict-free.
 constexpr int CW_GB = 8;                // groups per scale batch in LDS
-constexpr int CW_TPB = 4;               // row tiles per block (maxima pass)
 constexpr int CW_TPB_CAST = 1;          // row tiles per block (cast pass)
 constexpr int CW_GLDS = 2048;           // groups whose offsets are staged in LDS
 
@@ -132,14 +131,14 @@ __global__ void cw_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
 // ROWP: also write each row's maximum over the tile's 64 columns (bf16 magnitude bits) to
 // rowp[blockIdx.y * Rp + r] (Rp = R rounded up to 8; each lane of a row group stores its 8
 // consecutive rows at once): the dual-layout call reduces them into rowwise scales.
-template <bool VEC, bool LDS, bool NT, bool ROWP = false>
+template <bool VEC, bool LDS, bool NT, bool ROWP, int TPB>
 __global__ __launch_bounds__(256) void colwise_amax_kernel(const uint16_t* __restrict__ x,
                                                            int64_t R, int64_t C, int64_t ld_x,
                                                            const int32_t* __restrict__ offsets,
                                                            int G, uint32_t* __restrict__ amax,
                                                            uint16_t* __restrict__ rowp) {
     const int t = threadIdx.x, o = t & 7, qd = t >> 3, lane = t & 63, wave = t >> 6;
-    const int64_t rb = (int64_t)blockIdx.x * CW_TR * CW_TPB, c0 = (int64_t)blockIdx.y * CW_TC;
+    const int64_t rb = (int64_t)blockIdx.x * CW_TR * TPB, c0 = (int64_t)blockIdx.y * CW_TC;
     __shared__ uint32_t red[4][8][4];
     const Offs<LDS> off = stage_offsets<LDS>(offsets, G);
     // running per-lane maxima of group cur_g (block-uniform), published when the group ends
@@ -175,10 +174,10 @@ __global__ __launch_bounds__(256) void colwise_amax_kernel(const uint16_t* __res
     };
     uint4 v[8], vn[8];
     cw_load<VEC, NT>(x, R, C, ld_x, rb, c0, o, qd, v);
-    for (int k = 0; k < CW_TPB; k++) {
+    for (int k = 0; k < TPB; k++) {
         const int64_t r0 = rb + (int64_t)k * CW_TR;
         if (r0 >= R) break;  // block-uniform
-        if (k + 1 < CW_TPB) cw_load<VEC, NT>(x, R, C, ld_x, r0 + CW_TR, c0, o, qd, vn);
+        if (k + 1 < TPB) cw_load<VEC, NT>(x, R, C, ld_x, r0 + CW_TR, c0, o, qd, vn);
         const int64_t r_end = r0 + CW_TR < R ? r0 + CW_TR : R;
         if (ROWP) {
             // the 8 lanes of a row group (o = 0..7, consecutive lanes) hold its 64 columns;
@@ -653,6 +652,34 @@ static inline void wdual_layout(int64_t E, int64_t K, int64_t N, size_t& o_offs,
     total = o_part + up((size_t)E * (size_t)nb * (size_t)N * 2);
 }
 
+// The maxima pass walks TPB consecutive row tiles per block (the next tile's loads in flight
+// while one is reduced; fewer blocks, fewer atomics): 4, unless that leaves fewer than
+// CW_AMAX_MIN_BLOCKS blocks to hide the loads' latency (then 2, or 1).  dsv3 X^T (16384 x 7168,
+// one tile per block): 134 -> 126 us, dual-layout X 170 -> 161 us against 4 tiles per block.
+constexpr int64_t CW_AMAX_MIN_BLOCKS = 4096;
+static int amax_tpb(int64_t R, int64_t C) {
+    const int64_t strips = (C + CW_TC - 1) / CW_TC;
+    for (int tp = 4; tp > 1; tp >>= 1)
+        if ((R + CW_TR * tp - 1) / (CW_TR * tp) * strips >= CW_AMAX_MIN_BLOCKS) return tp;
+    return 1;
+}
+template <bool VEC, bool LDS, bool NT, bool ROWP>
+static void launch_amax(int tpb, const uint16_t* x, int64_t R, int64_t C, int64_t ld_x,
+                        const int32_t* offsets, int G, uint32_t* amax, uint16_t* rowp,
+                        hipStream_t stream) {
+    const unsigned gy = (unsigned)((C + CW_TC - 1) / CW_TC);
+    auto gx = [&](int tp) { return (unsigned)((R + CW_TR * tp - 1) / (CW_TR * tp)); };
+    if (tpb == 1)
+        colwise_amax_kernel<VEC, LDS, NT, ROWP, 1><<<dim3(gx(1), gy), dim3(256), 0, stream>>>(
+            x, R, C, ld_x, offsets, G, amax, rowp);
+    else if (tpb == 2)
+        colwise_amax_kernel<VEC, LDS, NT, ROWP, 2><<<dim3(gx(2), gy), dim3(256), 0, stream>>>(
+            x, R, C, ld_x, offsets, G, amax, rowp);
+    else
+        colwise_amax_kernel<VEC, LDS, NT, ROWP, 4><<<dim3(gx(4), gy), dim3(256), 0, stream>>>(
+            x, R, C, ld_x, offsets, G, amax, rowp);
+}
+
 template <int FMT>
 static fp8q_status_t colwise_run(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x,
                                  const int32_t* offsets, int G, uint8_t* qt, int64_t ld_qt,
@@ -679,25 +706,24 @@ static fp8q_status_t colwise_run(const uint16_t* x, int64_t R, int64_t C, int64_
     if (zb > 4096) zb = 4096;
     cw_zero_kernel<<<dim3((unsigned)zb), dim3(256), 0, stream>>>(ws, n);
     if (R > 0) {
-        const dim3 grid((unsigned)((R + CW_TR * CW_TPB - 1) / (CW_TR * CW_TPB)),
-                        (unsigned)((C + CW_TC - 1) / CW_TC));
         const bool lds = G <= CW_GLDS;
         // The cast pass reads the input again.  An input of up to 128 MB can stay in the 256 MB
         // last-level cache until then, so this pass reads it with ordinary loads; a larger one
         // cannot, and is read with streaming loads.
         const bool nt = (double)R * (double)ld_x * 2.0 > kStreamBytes;
+        const int tpb = amax_tpb(R, C);
         if (vec && lds && nt)
-            colwise_amax_kernel<true, true, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws, nullptr);
+            launch_amax<true, true, true, false>(tpb, x, R, C, ld_x, offsets, G, ws, nullptr, stream);
         else if (vec && lds)
-            colwise_amax_kernel<true, true, false><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws, nullptr);
+            launch_amax<true, true, false, false>(tpb, x, R, C, ld_x, offsets, G, ws, nullptr, stream);
         else if (vec && nt)
-            colwise_amax_kernel<true, false, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws, nullptr);
+            launch_amax<true, false, true, false>(4, x, R, C, ld_x, offsets, G, ws, nullptr, stream);
         else if (vec)
-            colwise_amax_kernel<true, false, false><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws, nullptr);
+            launch_amax<true, false, false, false>(4, x, R, C, ld_x, offsets, G, ws, nullptr, stream);
         else if (lds)
-            colwise_amax_kernel<false, true, false><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws, nullptr);
+            launch_amax<false, true, false, false>(4, x, R, C, ld_x, offsets, G, ws, nullptr, stream);
         else
-            colwise_amax_kernel<false, false, false><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, ws, nullptr);
+            launch_amax<false, false, false, false>(4, x, R, C, ld_x, offsets, G, ws, nullptr, stream);
     }
     if (vec && vec_out) launch_cast<FMT, true, true>(x, R, C, ld_x, offsets, G, ws, qt, ld_qt, s, stream);
     else if (vec) launch_cast<FMT, true, false>(x, R, C, ld_x, offsets, G, ws, qt, ld_qt, s, stream);
@@ -783,24 +809,24 @@ static fp8q_status_t dual_run(const uint16_t* x, int64_t R, int64_t C, int64_t l
     if (zb > 4096) zb = 4096;
     cw_zero_kernel<<<dim3((unsigned)zb), dim3(256), 0, stream>>>(amax, n);
     if (R > 0) {
-        const dim3 grid((unsigned)((R + CW_TR * CW_TPB - 1) / (CW_TR * CW_TPB)),
-                        (unsigned)((C + CW_TC - 1) / CW_TC));
+        const unsigned strips = (unsigned)((C + CW_TC - 1) / CW_TC);
         // the cast pass re-reads the input: streaming loads only past the last-level cache size
         const bool nt = (double)R * (double)ld_x * 2.0 > kStreamBytes;
+        const int tpb = amax_tpb(R, C);
         if (vec && lds && nt)
-            colwise_amax_kernel<true, true, true, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, amax, rowp);
+            launch_amax<true, true, true, true>(tpb, x, R, C, ld_x, offsets, G, amax, rowp, stream);
         else if (vec && lds)
-            colwise_amax_kernel<true, true, false, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, amax, rowp);
+            launch_amax<true, true, false, true>(tpb, x, R, C, ld_x, offsets, G, amax, rowp, stream);
         else if (vec && nt)
-            colwise_amax_kernel<true, false, true, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, amax, rowp);
+            launch_amax<true, false, true, true>(4, x, R, C, ld_x, offsets, G, amax, rowp, stream);
         else if (vec)
-            colwise_amax_kernel<true, false, false, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, amax, rowp);
+            launch_amax<true, false, false, true>(4, x, R, C, ld_x, offsets, G, amax, rowp, stream);
         else if (lds)
-            colwise_amax_kernel<false, true, false, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, amax, rowp);
+            launch_amax<false, true, false, true>(4, x, R, C, ld_x, offsets, G, amax, rowp, stream);
         else
-            colwise_amax_kernel<false, false, false, true><<<grid, dim3(256), 0, stream>>>(x, R, C, ld_x, offsets, G, amax, rowp);
+            launch_amax<false, false, false, true>(4, x, R, C, ld_x, offsets, G, amax, rowp, stream);
         dual_rowscale_kernel<FMT><<<dim3((unsigned)((R + 63) / 64)), dim3(256), 0, stream>>>(
-            rowp, R, (int)grid.y, s_rows);
+            rowp, R, (int)strips, s_rows);
     }
     if (vec && vec_out && lds)
         launch_cast_dual<FMT, true, true, true>(x, R, C, ld_x, offsets, G, amax, qt, ld_qt, s_cols, s_rows, q, ld_q, rowq_vec, stream);
