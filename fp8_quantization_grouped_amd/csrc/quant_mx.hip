@@ -67,10 +67,11 @@ __global__ __launch_bounds__(256) void mx_colwise_kernel(const uint16_t* __restr
                                                          int64_t R, int64_t C, int64_t ld_x,
                                                          uint8_t* __restrict__ qt, int64_t ld_qt,
                                                          uint8_t* __restrict__ e8, int64_t ld_s,
-                                                         bool vec_out, bool nt_out) {
+                                                         bool vec_out, bool nt_out, bool vec_e8) {
     const int t = threadIdx.x, o = t & 7, qd = t >> 3;
     const int64_t r0 = (int64_t)blockIdx.x * MXC_TR, c0 = (int64_t)blockIdx.y * MXC_TC;
     __shared__ __align__(16) uint8_t tile[MXC_TC * MXC_STR];
+    __shared__ __align__(8) uint8_t se8[MXC_TC * 8];  // [column][32-row block] of this tile
     const int64_t c = c0 + 8 * o;
     uint4 v[8];
 #pragma unroll
@@ -102,13 +103,12 @@ __global__ __launch_bounds__(256) void mx_colwise_kernel(const uint16_t* __restr
         inv[2 * d] = mx_inv_scale(eb[2 * d]);
         inv[2 * d + 1] = mx_inv_scale(eb[2 * d + 1]);
     }
+    // the block's E8M0 bytes go to LDS and leave as one 8-byte piece per column (a column's 8
+    // blocks of this tile are consecutive in its scale row) instead of 8 scattered byte stores
+    // per lane
     if ((qd & 3) == 0) {
-        const int64_t rb = (r0 + 8 * qd) / 32;
-        if (r0 + 8 * qd < R) {
 #pragma unroll
-            for (int j = 0; j < 8; j++)
-                if (c + j < C) e8[(c + j) * ld_s + rb] = (uint8_t)eb[j];
-        }
+        for (int j = 0; j < 8; j++) se8[(8 * o + j) * 8 + (qd >> 2)] = (uint8_t)eb[j];
     }
 #pragma unroll
     for (int j = 0; j < 8; j++) {
@@ -123,6 +123,15 @@ __global__ __launch_bounds__(256) void mx_colwise_kernel(const uint16_t* __restr
         *reinterpret_cast<uint2*>(&tile[(8 * o + j) * MXC_STR + 8 * (qd ^ (2 * o))]) = make_uint2(w0, w1);
     }
     __syncthreads();
+    if (t < MXC_TC && c0 + t < C) {
+        const int nb = R - r0 < MXC_TR ? (int)((R - r0) / 32) : MXC_TR / 32;  // R % 32 == 0
+        uint8_t* dst = e8 + (c0 + t) * ld_s + r0 / 32;
+        if (vec_e8 && nb == MXC_TR / 32) {
+            *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(&se8[t * 8]);
+        } else {
+            for (int b = 0; b < nb; b++) dst[b] = se8[t * 8 + b];
+        }
+    }
 #pragma unroll
     for (int k = 0; k < 4; k++) {
         const int ch = t + 256 * k;
@@ -176,9 +185,10 @@ extern "C" fp8q_status_t fp8_mx_quant_colwise(const uint16_t* x, int64_t rows, i
     const int64_t ct = (cols + fp8q::MXC_TC - 1) / fp8q::MXC_TC;
     if (rt > 0x7FFFFFFFLL || ct > 65535) return FP8Q_ERR_UNSUPPORTED;
     const bool vec_out = (ld_qt % 16 == 0) && fp8q_aligned(q_t, 16);
+    const bool vec_e8 = (ld_s % 8 == 0) && fp8q_aligned(e8m0, 8);  // tiles start at 8-block steps
     fp8q::mx_colwise_kernel<<<dim3((unsigned)rt, (unsigned)ct), dim3(256), 0, stream>>>(
         x, rows, cols, ld_x, q_t, ld_qt, e8m0, ld_s, vec_out,
-        (double)cols * (double)ld_qt > fp8q::kStreamBytes);
+        (double)cols * (double)ld_qt > fp8q::kStreamBytes, vec_e8);
     FP8Q_CHECK_LAUNCH();
     return FP8Q_OK;
 }
